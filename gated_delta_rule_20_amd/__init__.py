@@ -1,0 +1,212 @@
+"""MI355X-native Kimi Delta Attention (KDA) core.
+
+A thin ctypes binding over ``libkda.so`` (C ABI in ``include/kda.h``).  It
+only marshals arguments: every step of the computation runs in the HIP
+kernels.  PyTorch supplies device memory and the current stream.  There is no
+fallback: if the library is missing or the tensors are not on a ROCm device,
+the calls raise.
+
+"Kimi K3 Technical Report: Open Frontier Intelligence", §2.1.1 eq. (1) (the
+recurrence), eqs. (3)-(4) (chunkwise form), eq. (5) (gate).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_workspace_size", "load_library",
+           "KDAError", "LIB_PATH", "EXPORTED_SYMBOLS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+EXPORTED_SYMBOLS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_recurrent_step",
+                    "kda_status_string", "kda_last_error_message")
+
+KDA_F32, KDA_BF16 = 0, 1
+_DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+
+class KDAError(RuntimeError):
+    """A kda_* call returned a non-success status."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+class ChunkFwdArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("g_min", ctypes.c_float), ("scale", ctypes.c_float),
+                ("cu_seqlens", ctypes.c_void_p), ("N", ctypes.c_int32),
+                ("initial_state", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("final_state", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class StepArgs(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("H", ctypes.c_int32), ("Dk", ctypes.c_int32),
+                ("Dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("g_min", ctypes.c_float), ("scale", ctypes.c_float),
+                ("state", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} not found: build it with gated_delta_rule_20_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    lib.kda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkFwdArgs), ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkFwdArgs), ctypes.c_void_p]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_recurrent_step.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_void_p]
+    lib.kda_recurrent_step.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error_message.argtypes = []
+    lib.kda_last_error_message.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(lib, fn, status):
+    if status != 0:
+        raise KDAError(fn, status, lib.kda_last_error_message().decode() or
+                       lib.kda_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _chunk_args(q, k, v, g, beta, A_log, g_min, scale, cu_seqlens, N, h0, o, hT, ws, ws_bytes):
+    if cu_seqlens is not None:
+        T, H, Dk = q.shape[-3:]
+        B = 1
+    else:
+        B, T, H, Dk = q.shape
+    a = ChunkFwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, Dk, v.shape[-1]
+    a.dtype = _DTYPES[q.dtype]
+    a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
+    a.A_log = _ptr(A_log)
+    a.g_min, a.scale = float(g_min), float(scale)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.N = int(N)
+    a.initial_state, a.o, a.final_state = _ptr(h0), _ptr(o), _ptr(hT)
+    a.workspace, a.workspace_bytes = _ptr(ws), int(ws_bytes)
+    return a
+
+
+def chunk_fwd_workspace_size(q, v, *, cu_seqlens=None, N=None) -> int:
+    """Workspace bytes kda_chunk_fwd needs for q [B,T,H,Dk] (or [T,H,Dk] with
+    cu_seqlens) and v [..., Dv]."""
+    lib = load_library()
+    n = (cu_seqlens.numel() - 1) if cu_seqlens is not None else 0
+    a = _chunk_args(q, q, v, q, q, None, -5.0, 1.0, cu_seqlens, N if N is not None else n,
+                    None, None, None, None, 0)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    out = ctypes.c_size_t(0)
+    _check(lib, "kda_chunk_fwd_workspace_size", lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(out)))
+    return out.value
+
+
+def chunk_fwd(q, k, v, g, beta, *, A_log=None, g_min: float = -5.0, scale: float = 1.0,
+              cu_seqlens=None, initial_state=None, output_final_state: bool = True,
+              out=None, final_state=None, workspace=None, stream=None):
+    """Chunkwise-parallel KDA forward.
+
+    q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H] (bf16 or fp32).
+    With cu_seqlens ([N+1] int32 on device) the token axis is packed: pass
+    [T, H, D] / [T, H] (or with a leading 1).  ``g`` holds log-decays, or
+    decay logits z when ``A_log`` ([H] fp32) is given (eq. (5) gate in-kernel).
+    initial_state / final_state: [N, H, Dk, Dv] fp32 (final_state may be the
+    same tensor as initial_state for in-place resume).
+    Returns (o, final_state or None).
+    """
+    lib = load_library()
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _dev(t, name, q.dtype)
+    _dev(A_log, "A_log", torch.float32)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    _dev(initial_state, "initial_state", torch.float32)
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+        H, Dk = q.shape[-2:]
+    else:
+        N = q.shape[0]
+        H, Dk = q.shape[2], q.shape[3]
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    _dev(out, "out", q.dtype)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _dev(final_state, "final_state", torch.float32)
+    need = chunk_fwd_workspace_size(q, v, cu_seqlens=cu_seqlens, N=N)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a = _chunk_args(q, k, v, g, beta, A_log, g_min, scale, cu_seqlens, N, initial_state,
+                    out, final_state, workspace, ws_bytes)
+    _check(lib, "kda_chunk_fwd", lib.kda_chunk_fwd(ctypes.byref(a), _stream(stream, q.device)))
+    return out, final_state
+
+
+def recurrent_step(q, k, v, g, beta, state, *, A_log=None, g_min: float = -5.0,
+                   scale: float = 1.0, out=None, stream=None):
+    """One decode token per sequence, state [N, H, Dk, Dv] fp32 updated in
+    place.  q, k, g: [N, H, Dk]; v: [N, H, Dv]; beta: [N, H].  Returns o."""
+    lib = load_library()
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _dev(t, name, q.dtype)
+    _dev(state, "state", torch.float32)
+    _dev(A_log, "A_log", torch.float32)
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
+    _dev(out, "out", q.dtype)
+    a = StepArgs()
+    a.N, a.H, a.Dk, a.Dv, a.dtype = N, H, Dk, Dv, _DTYPES[q.dtype]
+    a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
+    a.A_log = _ptr(A_log)
+    a.g_min, a.scale = float(g_min), float(scale)
+    a.state, a.o = _ptr(state), _ptr(out)
+    _check(lib, "kda_recurrent_step", lib.kda_recurrent_step(ctypes.byref(a), _stream(stream, q.device)))
+    return out

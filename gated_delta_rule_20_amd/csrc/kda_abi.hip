@@ -1,0 +1,182 @@
+// kda_abi.hip -- the C ABI declared in include/kda.h: argument validation,
+// workspace planning and kernel dispatch.  Every check runs before anything
+// is enqueued; nothing here allocates device memory or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "kda.h"
+#include "kda_prefill.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kda_status_t fail(kda_status_t st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+kda_status_t check_common(int dtype, int Dk, int Dv, const float *A_log, float g_min)
+{
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERROR_INVALID_VALUE, "dtype %d is not a kda_dtype_t", dtype);
+    if (!head_dim_ok(Dk) || !head_dim_ok(Dv))
+        return fail(KDA_ERROR_NOT_SUPPORTED, "head dims Dk=%d Dv=%d: each must be 64 or 128", Dk, Dv);
+    if (!(g_min >= -5.0f && g_min < 0.0f))
+        return fail(KDA_ERROR_NOT_SUPPORTED, "g_min=%g: must lie in [-5, 0) for the sub-tile range bound", (double)g_min);
+    if (A_log && ((uintptr_t)A_log & 3u)) return fail(KDA_ERROR_INVALID_VALUE, "A_log is not 4-byte aligned");
+    return KDA_SUCCESS;
+}
+
+struct ChunkPlan {
+    int varlen, N, rows;
+    int n_chunks_cap;
+    size_t table, block, total;
+};
+
+kda_status_t plan_chunk(const kda_chunk_fwd_args_t *a, ChunkPlan *pl)
+{
+    if (!a) return fail(KDA_ERROR_INVALID_VALUE, "args is NULL");
+    kda_status_t st = check_common(a->dtype, a->Dk, a->Dv, a->A_log, a->g_min);
+    if (st != KDA_SUCCESS) return st;
+    if (a->B < 1 || a->T < 0 || a->H < 1)
+        return fail(KDA_ERROR_INVALID_VALUE, "need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)", a->B, a->T, a->H);
+    const size_t block = kda::block_bytes(a->dtype == KDA_BF16, a->Dk, a->Dv);
+    if (block == 0)
+        return fail(KDA_ERROR_NOT_SUPPORTED, "prefill with float32 inputs supports Dk=Dv=64 only (got Dk=%d Dv=%d)",
+                    a->Dk, a->Dv);
+    pl->varlen = a->cu_seqlens != nullptr;
+    if (pl->varlen) {
+        if (a->B != 1) return fail(KDA_ERROR_INVALID_VALUE, "cu_seqlens requires B == 1 (got B=%d)", a->B);
+        if (a->N < 1) return fail(KDA_ERROR_INVALID_VALUE, "cu_seqlens requires N >= 1 (got N=%d)", a->N);
+        if ((uintptr_t)a->cu_seqlens & 3u) return fail(KDA_ERROR_INVALID_VALUE, "cu_seqlens is not 4-byte aligned");
+        pl->N = a->N;
+    } else {
+        pl->N = a->B;
+    }
+    const long long rows = (long long)a->B * a->T;
+    if (rows > 0x7fffffffLL || (long long)pl->N * a->H > 0x0fffffffLL)
+        return fail(KDA_ERROR_NOT_SUPPORTED, "problem too large for 32-bit token/pair indices");
+    pl->rows = (int)rows;
+    const long long cap = pl->varlen ? (long long)a->T / KDA_CHUNK + pl->N
+                                     : (long long)a->B * ((a->T + KDA_CHUNK - 1) / KDA_CHUNK);
+    if (cap > 0x7fffffffLL) return fail(KDA_ERROR_NOT_SUPPORTED, "too many chunks");
+    pl->n_chunks_cap = (int)cap;
+    pl->table = kda::table_bytes(pl->varlen, pl->N);
+    pl->block = block;
+    pl->total = pl->table + (size_t)a->H * (size_t)cap * block;
+    return KDA_SUCCESS;
+}
+
+kda_status_t hip_fail(hipError_t e, const char *what)
+{
+    return fail(KDA_ERROR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status_t s)
+{
+    switch (s) {
+    case KDA_SUCCESS: return "success";
+    case KDA_ERROR_INVALID_VALUE: return "invalid value";
+    case KDA_ERROR_NOT_SUPPORTED: return "not supported";
+    case KDA_ERROR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERROR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *kda_last_error_message(void) { return g_err; }
+
+kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args_t *a, size_t *bytes)
+{
+    if (!bytes) return fail(KDA_ERROR_INVALID_VALUE, "bytes is NULL");
+    ChunkPlan pl;
+    const kda_status_t st = plan_chunk(a, &pl);
+    if (st != KDA_SUCCESS) return st;
+    *bytes = pl.total;
+    g_err[0] = 0;
+    return KDA_SUCCESS;
+}
+
+kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *a, void *stream)
+{
+    ChunkPlan pl;
+    kda_status_t st = plan_chunk(a, &pl);
+    if (st != KDA_SUCCESS) return st;
+    const bool has_tokens = pl.rows > 0;
+    if (has_tokens) {
+        const void *req[] = {a->q, a->k, a->v, a->g, a->beta, a->o};
+        const char *nm[] = {"q", "k", "v", "g", "beta", "o"};
+        for (int i = 0; i < 6; ++i) {
+            if (!req[i]) return fail(KDA_ERROR_INVALID_VALUE, "%s is NULL", nm[i]);
+            if (i != 4 && !aligned16(req[i])) return fail(KDA_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", nm[i]);
+        }
+        if ((uintptr_t)a->beta & (a->dtype == KDA_BF16 ? 1u : 3u))
+            return fail(KDA_ERROR_INVALID_VALUE, "beta is not aligned to its element size");
+    }
+    if (a->initial_state && !aligned16(a->initial_state))
+        return fail(KDA_ERROR_INVALID_VALUE, "initial_state is not 16-byte aligned");
+    if (a->final_state && !aligned16(a->final_state))
+        return fail(KDA_ERROR_INVALID_VALUE, "final_state is not 16-byte aligned");
+    if (pl.total > 0) {
+        if (!a->workspace) return fail(KDA_ERROR_WORKSPACE, "workspace is NULL but %zu bytes are needed", pl.total);
+        if (a->workspace_bytes < pl.total)
+            return fail(KDA_ERROR_WORKSPACE, "workspace has %zu bytes, needs %zu", a->workspace_bytes, pl.total);
+        if ((uintptr_t)a->workspace & 255u) return fail(KDA_ERROR_WORKSPACE, "workspace is not 256-byte aligned");
+    }
+    if (!has_tokens && !a->final_state) {  // nothing observable to compute
+        g_err[0] = 0;
+        return KDA_SUCCESS;
+    }
+
+    kda::PrefillParams p;
+    p.q = a->q; p.k = a->k; p.v = a->v; p.g = a->g; p.beta = a->beta;
+    p.A_log = a->A_log; p.g_min = a->g_min; p.scale = a->scale;
+    p.cu = a->cu_seqlens; p.N = pl.N; p.T = a->T; p.H = a->H; p.varlen = pl.varlen;
+    p.h0 = a->initial_state; p.hT = a->final_state; p.o = a->o;
+    char *ws = (char *)a->workspace;
+    p.chunk_off = pl.varlen ? (int32_t *)ws : nullptr;
+    p.order = pl.varlen ? (int32_t *)ws + (pl.N + 1) : nullptr;
+    p.blocks = ws ? ws + pl.table : nullptr;
+    p.n_chunks_cap = has_tokens ? pl.n_chunks_cap : 0;
+    const hipError_t e = kda::launch_chunk_fwd(a->dtype == KDA_BF16, a->Dk, a->Dv, p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
+    g_err[0] = 0;
+    return KDA_SUCCESS;
+}
+
+kda_status_t kda_recurrent_step(const kda_step_args_t *a, void *stream)
+{
+    if (!a) return fail(KDA_ERROR_INVALID_VALUE, "args is NULL");
+    kda_status_t st = check_common(a->dtype, a->Dk, a->Dv, a->A_log, a->g_min);
+    if (st != KDA_SUCCESS) return st;
+    if (a->N < 0 || a->H < 1) return fail(KDA_ERROR_INVALID_VALUE, "need N >= 0, H >= 1 (got N=%d H=%d)", a->N, a->H);
+    if ((long long)a->N * a->H > 0x7fffffffLL) return fail(KDA_ERROR_NOT_SUPPORTED, "N*H too large");
+    if (a->N == 0) { g_err[0] = 0; return KDA_SUCCESS; }
+    const void *req[] = {a->q, a->k, a->v, a->g, a->beta, a->state, a->o};
+    const char *nm[] = {"q", "k", "v", "g", "beta", "state", "o"};
+    for (int i = 0; i < 7; ++i) {
+        if (!req[i]) return fail(KDA_ERROR_INVALID_VALUE, "%s is NULL", nm[i]);
+        if (i != 4 && !aligned16(req[i])) return fail(KDA_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", nm[i]);
+    }
+    if ((uintptr_t)a->beta & (a->dtype == KDA_BF16 ? 1u : 3u))
+        return fail(KDA_ERROR_INVALID_VALUE, "beta is not aligned to its element size");
+    const hipError_t e = kda::launch_recurrent_step(a->dtype == KDA_BF16, a->N, a->H, a->Dk, a->Dv, a->q, a->k,
+                                                    a->v, a->g, a->beta, a->A_log, a->g_min, a->scale, a->state,
+                                                    a->o, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kda_recurrent_step launch");
+    g_err[0] = 0;
+    return KDA_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// kda_prefill.h -- host-side interface of the chunkwise-parallel KDA kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Everything the three prefill kernels need, passed by value.
+struct PrefillParams {
+    const void *q, *k, *v, *g, *beta;   // [rows, H, D] token-major, element type T
+    const float *A_log;                 // [H] or null (g holds log-decays)
+    float g_min, scale;
+    const int32_t *cu;                  // [N+1] packed-sequence offsets (varlen) or null
+    int N, T, H;                        // N sequences; T = tokens per sequence when !varlen
+    int varlen;
+    const float *h0;                    // [N, H, Dk, Dv] or null
+    float *hT;                          // [N, H, Dk, Dv] or null
+    void *o;                            // [rows, H, Dv]
+    int32_t *chunk_off;                 // [N+1] (varlen; workspace)
+    int32_t *order;                     // [N]   (varlen; workspace)
+    char *blocks;                       // [H][n_chunks_cap] per-chunk blocks (workspace)
+    int n_chunks_cap;
+};
+
+// Bytes of one (head, chunk) workspace block; 0 if the combination is unsupported.
+size_t block_bytes(int bf16, int Dk, int Dv);
+
+// Bytes of the chunk table at the front of the workspace (0 when !varlen).
+inline size_t table_bytes(int varlen, int N)
+{
+    return varlen ? ((size_t)(2 * N + 1) * sizeof(int32_t) + 255) / 256 * 256 : 0;
+}
+
+// Enqueue the full prefill on `stream`.  The caller has validated arguments
+// and carved the workspace into p.chunk_off / p.order / p.blocks.
+hipError_t launch_chunk_fwd(int bf16, int Dk, int Dv, const PrefillParams &p, hipStream_t stream);
+
+hipError_t launch_recurrent_step(int bf16, int N, int H, int Dk, int Dv, const void *q,
+                                 const void *k, const void *v, const void *g, const void *beta,
+                                 const float *A_log, float g_min, float scale, float *state,
+                                 void *o, hipStream_t stream);
+
+}  // namespace kda

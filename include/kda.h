@@ -1,0 +1,141 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) core.
+ *
+ * What is computed: "Kimi K3 Technical Report: Open Frontier Intelligence",
+ * §2.1.1 (Kimi Delta Attention).  Per head, with state S in R^{d_k x d_v}:
+ *
+ *   eq. (1)   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *             o_t = S_t^T (scale * q_t)                (eq. (1) itself has scale = 1)
+ *   eq. (5)   g_t = g_min * Sigmoid(exp(A_h) * z_t),  alpha_t = exp(g_t)
+ *
+ * kda_chunk_fwd evaluates eq. (1) over whole sequences in the chunkwise-parallel
+ * form of eqs. (3)-(4) (chunk size 64, 16-token sub-tiles); kda_recurrent_step
+ * applies eq. (1) to one token per sequence with the state updated in place
+ * (§5.4.2, "KDA" paragraph: the decode state is updated in place every step).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; all tensors are
+ *     dense, row-major (last index fastest) and 16-byte aligned.  The library
+ *     allocates no device memory and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *     No call synchronises the device or copies data to the host.
+ *   - Validation happens before anything is enqueued; on error nothing is
+ *     launched and no output is touched.  A launch failure returns
+ *     KDA_ERROR_HIP; faults during execution surface at the caller's next
+ *     synchronisation, as usual for HIP.  kda_last_error_message() returns a
+ *     thread-local description of the last failure on the calling thread.
+ *   - Decay input `g`: when A_log is NULL it holds log-decays g in [g_min, 0]
+ *     (values outside are clamped to that range, which the range argument of
+ *     eq. (5) needs); when A_log is non-NULL it holds decay logits z and the
+ *     eq. (5) gate is applied inside the kernels in fp32.
+ *   - Preconditions not checked on the device: q and k rows have L2 norm <= 1
+ *     (eq. (2) normalises them), beta in [0, 1], cu_seqlens non-decreasing
+ *     from 0 to T.
+ *   - The library is thread-safe; calls that share output buffers race.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define KDA_API __attribute__((visibility("default")))
+#else
+#define KDA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_F32 = 0,   /* float32 q, k, v, g, beta, o */
+    KDA_BF16 = 1   /* bfloat16 q, k, v, g, beta, o (fp32 state and accumulation) */
+} kda_dtype_t;
+
+typedef enum {
+    KDA_SUCCESS = 0,
+    KDA_ERROR_INVALID_VALUE = 1,   /* null pointer, bad size, misalignment, bad flag */
+    KDA_ERROR_NOT_SUPPORTED = 2,   /* head dims outside {64, 128}, g_min outside [-5, 0) */
+    KDA_ERROR_WORKSPACE = 3,       /* workspace missing or smaller than required */
+    KDA_ERROR_HIP = 4              /* a HIP runtime call or kernel launch failed */
+} kda_status_t;
+
+/* Chunk size of the chunkwise-parallel form and its sub-tile size. */
+#define KDA_CHUNK 64
+#define KDA_SUBTILE 16
+
+/*
+ * Prefill / training forward over whole sequences (chunkwise-parallel form,
+ * §2.1.1 eqs. (3)-(4); inter-chunk state hand-off derived from eq. (1)).
+ *
+ * Shapes (row-major):
+ *   q, k, g : [B, T, H, Dk]     v, o : [B, T, H, Dv]     beta : [B, T, H]
+ *   A_log   : [H] float32, or NULL (see "Decay input" above)
+ *   cu_seqlens : [N+1] int32 token offsets of N packed sequences, or NULL.
+ *                When set, B must be 1 and sequence s covers tokens
+ *                [cu_seqlens[s], cu_seqlens[s+1]) of the T tokens; chunks restart
+ *                at every sequence start.  When NULL, the B rows are the N = B
+ *                sequences, each T tokens long.
+ *   initial_state : [N, H, Dk, Dv] float32 entering states, or NULL for zeros.
+ *                   Read only; it may alias final_state (in-place resume).
+ *   final_state   : [N, H, Dk, Dv] float32 states after each sequence's last
+ *                   token, or NULL if not wanted.
+ * Dk, Dv in {64, 128}.  T may be 0 (then final_state = initial_state).
+ * The workspace (device memory, >= kda_chunk_fwd_workspace_size bytes,
+ * 256-byte aligned) holds per-chunk intermediates; its contents on entry are
+ * ignored and on exit are unspecified.
+ */
+typedef struct {
+    int32_t B, T, H, Dk, Dv;
+    int32_t dtype;                 /* kda_dtype_t */
+    const void *q, *k, *v, *g, *beta;
+    const float *A_log;
+    float g_min;                   /* lower bound of the log-decay, in [-5, 0); the pages use -5 */
+    float scale;                   /* query scale; 1.0 reproduces eq. (1) */
+    const int32_t *cu_seqlens;
+    int32_t N;                     /* number of sequences when cu_seqlens is set (else ignored) */
+    const float *initial_state;
+    void *o;
+    float *final_state;
+    void *workspace;
+    size_t workspace_bytes;
+} kda_chunk_fwd_args_t;
+
+/* Workspace bytes kda_chunk_fwd needs for these shapes (pointers are not read).
+ * Depends on B, T, H, Dk, Dv, dtype and on whether cu_seqlens is set (and N). */
+KDA_API kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args_t *args, size_t *bytes);
+
+KDA_API kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *args, void *stream);
+
+/*
+ * One decode step for N independent sequences (one token each), eq. (1):
+ *   q, k, g : [N, H, Dk]    v, o : [N, H, Dv]    beta : [N, H]
+ *   state   : [N, H, Dk, Dv] float32, read and overwritten IN PLACE with S_t.
+ * Dk, Dv in {64, 128}; A_log / g as for kda_chunk_fwd.
+ */
+typedef struct {
+    int32_t N, H, Dk, Dv;
+    int32_t dtype;                 /* kda_dtype_t */
+    const void *q, *k, *v, *g, *beta;
+    const float *A_log;
+    float g_min;
+    float scale;
+    float *state;
+    void *o;
+} kda_step_args_t;
+
+KDA_API kda_status_t kda_recurrent_step(const kda_step_args_t *args, void *stream);
+
+/* Static description of a status code. */
+KDA_API const char *kda_status_string(kda_status_t status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+KDA_API const char *kda_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

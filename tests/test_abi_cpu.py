@@ -1,0 +1,156 @@
+"""The C-ABI library loads and exports every symbol include/kda.h declares, and
+rejects bad arguments with a status before touching the device (CPU only:
+no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import gated_delta_rule_20_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_20_amd import build
+        build.build()
+    return kda.load_library()
+
+
+def _declared():
+    src = open(HEADER).read()
+    return set(re.findall(r"KDA_API\s+[\w\s\*]+?\b(kda_\w+)\s*\(", src))
+
+
+def test_header_declarations_match_binding():
+    assert _declared() == set(kda.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for s, text in [(0, "success"), (1, "invalid value"), (2, "not supported"), (3, "workspace"), (4, "HIP")]:
+        assert text in lib.kda_status_string(s).decode()
+
+
+def _args(**over):
+    a = kda.ChunkFwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv, a.dtype = 1, 128, 2, 128, 128, kda.KDA_BF16
+    for f in ("q", "k", "v", "g", "beta", "o"):
+        setattr(a, f, 0x10000)
+    a.g_min, a.scale = -5.0, 1.0
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+def _ws(lib, a):
+    out = ctypes.c_size_t(0)
+    st = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_formula(lib):
+    st, n = _ws(lib, _args())
+    assert st == 0
+    block = 74240  # bf16, d=128: 3*64*128 + 64*64 + 64*128 elements + 128 fp32 gammas
+    assert n == 2 * 2 * block
+    st, n2 = _ws(lib, _args(T=129))
+    assert st == 0 and n2 == 2 * 3 * block
+    cu = 0x20000
+    st, n3 = _ws(lib, _args(T=1000, cu_seqlens=cu, N=5))
+    assert st == 0 and n3 == 256 + 2 * (1000 // 64 + 5) * block
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(Dk=96), 2, "head dims"),
+    (dict(Dv=32), 2, "head dims"),
+    (dict(dtype=7), 1, "dtype"),
+    (dict(g_min=-6.0), 2, "g_min"),
+    (dict(g_min=0.0), 2, "g_min"),
+    (dict(H=0), 1, "H >= 1"),
+    (dict(T=-1), 1, "T >= 0"),
+    (dict(dtype=kda.KDA_F32), 2, "float32"),
+    (dict(cu_seqlens=0x20000, B=2, N=2), 1, "B == 1"),
+    (dict(cu_seqlens=0x20000, N=0), 1, "N >= 1"),
+])
+def test_workspace_size_rejects(lib, over, status, msg):
+    st, _ = _ws(lib, _args(**over))
+    assert st == status
+    assert msg in lib.kda_last_error_message().decode()
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(o=None), 1, "o is NULL"),
+    (dict(k=0x10008), 1, "k is not 16-byte aligned"),
+    (dict(beta=0x10001), 1, "beta is not aligned"),
+    (dict(initial_state=0x10004), 1, "initial_state"),
+    (dict(workspace=None, workspace_bytes=0), 3, "workspace is NULL"),
+    (dict(workspace=0x100000, workspace_bytes=1024), 3, "needs"),
+    (dict(workspace=0x100010, workspace_bytes=1 << 30), 3, "256-byte"),
+])
+def test_chunk_fwd_rejects_before_launch(lib, over, status, msg):
+    a = _args(**over)
+    st = lib.kda_chunk_fwd(ctypes.byref(a), None)
+    assert st == status, lib.kda_last_error_message()
+    assert msg in lib.kda_last_error_message().decode()
+
+
+def test_chunk_fwd_rejects_null_args(lib):
+    assert lib.kda_chunk_fwd(None, None) == 1
+    out = ctypes.c_size_t(0)
+    assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(_args()), None) == 1
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(Dk=32), 2, "head dims"),
+    (dict(state=None), 1, "state is NULL"),
+    (dict(v=0x10002), 1, "v is not 16-byte aligned"),
+    (dict(H=0), 1, "H >= 1"),
+    (dict(g_min=-7.0), 2, "g_min"),
+])
+def test_recurrent_step_rejects_before_launch(lib, over, status, msg):
+    a = kda.StepArgs()
+    a.N, a.H, a.Dk, a.Dv, a.dtype = 4, 2, 128, 128, kda.KDA_BF16
+    for f in ("q", "k", "v", "g", "beta", "state", "o"):
+        setattr(a, f, 0x10000)
+    a.g_min, a.scale = -5.0, 1.0
+    for key, val in over.items():
+        setattr(a, key, val)
+    assert lib.kda_recurrent_step(ctypes.byref(a), None) == status
+    assert msg in lib.kda_last_error_message().decode()
+
+
+def test_recurrent_step_zero_sequences_is_a_noop(lib):
+    a = kda.StepArgs()
+    a.N, a.H, a.Dk, a.Dv, a.dtype, a.g_min = 0, 2, 128, 128, kda.KDA_BF16, -5.0
+    assert lib.kda_recurrent_step(ctypes.byref(a), None) == 0
+
+
+def test_python_binding_requires_device_tensors(lib):
+    x = torch.zeros(1, 8, 2, 64)
+    with pytest.raises(ValueError, match="device tensor"):
+        kda.chunk_fwd(x, x, x, x, torch.zeros(1, 8, 2))
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "gated_delta_rule_20_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src.replace("oracle/", ""), f
