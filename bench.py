@@ -1,0 +1,232 @@
+"""Benchmark of the KDA core on one MI355X.
+
+One step = one ``kda_chunk_fwd`` call over the prefill_8k workload (B=1,
+T=8192, H=32, d_k=d_v=128, chunk 64, bf16 q/k/v/z/beta, fp32 state) with its
+inputs already resident in HBM; three independent input sets rotate so no
+step reads the previous step's inputs from the 256 MB last-level cache.  The
+decode workload (512 sequences x 32 heads, fp32 state of 1 GiB updated in
+place, 64 steps with fresh inputs) is timed alongside.  Prints one JSON line.
+
+Roofline figures use algorithmic counts per (token, head) at d = 128, C = 64
+(derived from eq. (1) and the chunkwise form of eqs. (3)-(4) of "Kimi K3
+Technical Report: Open Frontier Intelligence" §2.1.1):
+  prefill bytes  = 5 x 256 (q, k, v, z, o in bf16) + 2 (beta) = 1282, plus the
+                   fp32 initial and final state per (sequence, head);
+  prefill FLOPs  = 6 d_k d_v + (3C - 1) d_k + 2C d_v = 139136;
+  decode bytes   = 2 x 64 KiB (fp32 state read + write) + 1282.
+Timing uses HIP events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gated_delta_rule_20_amd as kda  # noqa: E402
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix, published (no sparsity)
+METRIC = "KDA prefill tokens/s + % bf16 MFMA peak; decode state-update % HBM BW"
+
+
+def prefill_counts(T, H, Dk, Dv, N, C=64, elem=2):
+    per_tok_bytes = elem * (3 * Dk + 2 * Dv) + elem          # q, k, z, v, o + beta
+    state_bytes = 2 * N * H * Dk * Dv * 4                     # h0 read + hT write
+    flops = (6 * Dk * Dv + (3 * C - 1) * Dk + 2 * C * Dv) * T * H
+    return per_tok_bytes * T * H + state_bytes, flops
+
+
+def decode_counts(N, H, Dk, Dv, elem=2):
+    return N * H * (2 * Dk * Dv * 4 + elem * (3 * Dk + 2 * Dv) + elem), N * H * 7 * Dk * Dv
+
+
+def time_calls(fn, n, stream):
+    """Run fn(i) n times, each bracketed by HIP events on `stream`; returns
+    (per-call ms list, wall ms of the whole region)."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        starts[i].record(stream)
+        fn(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
+
+
+def bench_prefill(steps, warmup, n_sets=3):
+    w = W.WORKLOADS["prefill_8k"]
+    import dataclasses
+    sets = []
+    for i in range(n_sets):
+        inp = W.make_prefill(dataclasses.replace(w, seed=w.seed + 17 * i), device="cuda")
+        o = torch.empty_like(inp["v"])
+        hT = torch.empty_like(inp["h0"])
+        nws = kda.chunk_fwd_workspace_size(inp["q"], inp["v"])
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        sets.append((inp, o, hT, ws))
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        inp, o, hT, ws = sets[i % n_sets]
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["z"], inp["beta"], A_log=inp["A_log"],
+                      g_min=inp["g_min"], initial_state=inp["h0"], out=o, final_state=hT,
+                      workspace=ws, stream=stream)
+
+    for i in range(warmup):
+        call(i)
+    per_call, wall = time_calls(call, steps, stream)
+    B, T, H, Dk = sets[0][0]["q"].shape
+    Dv = sets[0][0]["v"].shape[-1]
+    nbytes, flops = prefill_counts(B * T, H, Dk, Dv, B)
+    ms = sum(per_call) / len(per_call)
+    return dict(ms=ms, ms_min=min(per_call), wall_ms=wall, tokens=B * T, bytes=nbytes, flops=flops,
+                inputs=sets[0][0], shape=(B, T, H, Dk, Dv))
+
+
+def bench_decode(warmup_rounds=1):
+    w = W.WORKLOADS["decode_512"]
+    d = W.make_decode(w, device="cuda")
+    state = d["state"]
+    steps = d["steps"]
+    outs = [torch.empty_like(st["v"]) for st in steps]
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        st = steps[i]
+        kda.recurrent_step(st["q"], st["k"], st["v"], st["z"], st["beta"], state, A_log=d["A_log"],
+                           g_min=d["g_min"], out=outs[i], stream=stream)
+
+    for _ in range(warmup_rounds):
+        for i in range(len(steps)):
+            call(i)
+    per_call, wall = time_calls(call, len(steps), stream)
+    N, H, Dk = steps[0]["q"].shape
+    Dv = steps[0]["v"].shape[-1]
+    nbytes, flops = decode_counts(N, H, Dk, Dv)
+    us = 1e3 * sum(per_call) / len(per_call)
+    return dict(us=us, us_min=1e3 * min(per_call), steps=len(steps), N=N, H=H, bytes=nbytes, flops=flops)
+
+
+def copy_calibration(steps, nbytes=1 << 30):
+    """A plain device-to-device copy of known size (for scaling the HBM
+    FETCH_SIZE / WRITE_SIZE counters: it reads and writes nbytes each)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    per_call, _ = time_calls(lambda i: dst.copy_(src), steps, stream)
+    ms = sum(per_call) / len(per_call)
+    return {"copy_bytes_each_way": nbytes, "ms": ms, "GBps_read_plus_write": 2 * nbytes / (ms / 1e3) / 1e9}
+
+
+def cpu_baseline(inp, max_threads=16):
+    """The fp64 oracle on the host cores, over the full prefill_8k input set
+    (best of two runs).  Reported baseline only."""
+    import oracle
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()[0]
+    q, k, v, z, b = (f64(inp[x]) for x in ("q", "k", "v", "z", "beta"))
+    h0 = inp["h0"].detach().to("cpu", torch.float64).numpy()
+    A = inp["A_log"].detach().to("cpu", torch.float64).numpy()
+    threads = min(max_threads, os.cpu_count() or 1)
+    best, used = None, threads
+    for _ in range(2):
+        t0 = time.perf_counter()
+        _, _, used = oracle.forward(q, k, v, z, b, h0=h0, A_log=A, g_min=inp["g_min"], nthreads=threads,
+                                    return_threads=True)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    T = q.shape[0]
+    return {"value": T / best, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"full prefill_8k workload ({T} tokens x {q.shape[1]} heads), fp64, best of 2 runs, "
+                      f"{best:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--mode", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="prefill/decode/copy run one part only (for profiler runs); the JSON line "
+                         "of the benchmark contract is printed in mode 'all'")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+    kda.load_library()
+    if args.mode == "copy":
+        print(json.dumps(copy_calibration(args.steps)))
+        return
+    if args.mode == "decode":
+        dc = bench_decode()
+        print(json.dumps({k: v for k, v in dc.items()}))
+        return
+
+    pf = bench_prefill(args.steps, args.warmup)
+    if args.mode == "prefill":
+        print(json.dumps({"ms": pf["ms"], "ms_min": pf["ms_min"], "tokens_per_s": pf["tokens"] / (pf["ms"] / 1e3)}))
+        return
+    sec = pf["ms"] / 1e3
+    achieved = pf["bytes"] / sec / 1e9
+    tflops = pf["flops"] / sec / 1e12
+    B, T, H, Dk, Dv = pf["shape"]
+    result = {
+        "metric": METRIC,
+        "value": pf["tokens"] / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill_8k: B={B} T={T} H={H} d_k={Dk} d_v={Dv} chunk=64, "
+                               "bf16 q/k/v/z/beta, fp32 initial+final state, eq.(5) gate in-kernel",
+                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd (intra_chunk_kernel + chain_kernel)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": pf["bytes"]},
+        "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops": pf["flops"]},
+        "prefill_ms_min": pf["ms_min"],
+        "prefill_wall_ms": pf["wall_ms"],
+    }
+    if not args.no_decode:
+        dc = bench_decode()
+        gbs = dc["bytes"] / (dc["us"] / 1e6) / 1e9
+        result["decode"] = {
+            "workload": f"decode_512: N={dc['N']} x 1 token, H={dc['H']}, d=128, fp32 state 1 GiB in place, "
+                        f"{dc['steps']} steps with fresh inputs",
+            "us_per_step": dc["us"], "us_min": dc["us_min"],
+            "tokens_per_s": dc["N"] / (dc["us"] / 1e6),
+            "roofline": {"bound": "hbm", "kernel": "recurrent_step_kernel", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": None, "algorithmic_bytes": dc["bytes"]},
+        }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(pf["inputs"])
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

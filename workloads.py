@@ -14,8 +14,9 @@ Open Frontier Intelligence" §2.1.1 notation, d_k = d_v = d):
 * ``prefill_128k``   as prefill_8k with T=131072, plus 5% of (head, channel)
                      decay channels driven to hard forgetting and 5% to
                      near-unit retention (see ``_force_channels``).
-* ``varlen_64``      64 packed sequences, lengths ~ U{128..16384}, H=32,
-                     d=128, per-sequence initial states.
+* ``varlen_64``      64 packed sequences, lengths ~ U{128..16384} (the
+                     length seed is picked so the total is ~530K tokens:
+                     530,033), H=32, d=128, per-sequence initial states.
 * ``decode_512``     512 sequences x 1 token per step, H=32, d=128, 64 steps
                      with fresh inputs, fp32 state [512, 32, 128, 128].
 
@@ -47,6 +48,7 @@ class Workload:
     T: int = 0                        # tokens per batch row (fixed-length)
     n_seqs: int = 0                   # varlen: number of packed sequences
     len_range: tuple = (0, 0)         # varlen: inclusive length range
+    len_seed: int = 0                 # varlen: seed of the length draw
     zero_h0: bool = False
     A_uniform: float = 0.0            # A_h ~ U(-a, a); 0 -> A_h = 0
     h0_std: float = 0.02
@@ -67,7 +69,7 @@ WORKLOADS = {
     "prefill_128k": Workload("prefill_128k", torch.bfloat16, H=32, Dk=128, Dv=128, seed=2,
                              B=1, T=131072, A_uniform=1.0, force_frac=0.05),
     "varlen_64": Workload("varlen_64", torch.bfloat16, H=32, Dk=128, Dv=128, seed=3,
-                          n_seqs=64, len_range=(128, 16384), A_uniform=1.0),
+                          n_seqs=64, len_range=(128, 16384), len_seed=247, A_uniform=1.0),
     "decode_512": Workload("decode_512", torch.bfloat16, H=32, Dk=128, Dv=128, seed=4,
                            B=512, T=1, decode_steps=64),
 }
@@ -111,9 +113,11 @@ def _force_channels(z, A, frac, gen, device):
 
 
 def varlen_lengths(w: Workload, device="cpu") -> torch.Tensor:
-    gen = _gen(w.seed, device)
+    """Sequence lengths ~ U{lo..hi}, drawn on the CPU so they do not depend
+    on the device; the seed is the workload's ``len_seed``."""
+    gen = _gen(w.len_seed, "cpu")
     lo, hi = w.len_range
-    return torch.randint(lo, hi + 1, (w.n_seqs,), generator=gen, device=device)
+    return torch.randint(lo, hi + 1, (w.n_seqs,), generator=gen).to(device)
 
 
 def make_prefill(w: Workload, device="cpu", T: int | None = None, H: int | None = None,
