@@ -39,6 +39,15 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 __device__ __forceinline__ int kmap(int g, int e) { return (e < 4) ? 4 * g + e : 12 + 4 * g + e; }
 
+// Storage position of index k when a k-axis is kept in kmap order (inverse of
+// kmap inside each block of 32): position 8g + e holds k = kmap(g, e).  Four
+// consecutive k starting at a multiple of 4 stay contiguous.
+__device__ __forceinline__ int kpos(int k)
+{
+    const int b = k & ~31, kk = k & 31;
+    return b + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
+}
+
 // ---- element type traits ---------------------------------------------------
 template <typename T> struct Elem;
 
@@ -127,6 +136,14 @@ template <typename T> __device__ __forceinline__ frag_t<T> load_frag_kmap(const 
 template <typename T> __device__ __forceinline__ frag_t<T> load_frag_lin(const T *row, int g) {
     return load8(row + 8 * g);
 }
+
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also waits for
+// every outstanding global load and store of the wave (vmcnt(0)), which would
+// drain register prefetches and in-flight result stores at each barrier; the
+// kernels never pass data between threads through global memory within a
+// launch, so waiting for this wave's LDS operations is sufficient.  The
+// "memory" clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 

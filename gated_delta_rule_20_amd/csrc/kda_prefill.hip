@@ -51,7 +51,7 @@ namespace kda {
 // kernel's wave index: token rows 16w..16w+15 of the chunk, and state rows
 // 16*RT*w .. 16*RT*(w+1)-1.  All fragments use kmap() along k.
 //   Wn  [4 waves][KS][64 lanes][8]  A-operand fragments of -W    (rows tokens, k channels)
-//   Qp  [4 waves][KS][64][8]        A-operand fragments of scale*Q*Gamma
+//   Qp  [4 waves][KS][64][8]        operand fragments of scale*Q*Gamma (rows tokens, k channels)
 //   Kt  [4 waves][RT][2][64][8]     A-operand fragments of (K*gamma^C/Gamma)^T (rows channels, k tokens)
 //   A   [4 waves][2][64][8]         A-operand fragments of A     (rows tokens, k tokens)
 //   U   [NS][4 waves][64][4]        accumulator quads of U
@@ -128,31 +128,141 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t *__rest
 }
 
 // -----------------------------------------------------------------------------
-// Intra-chunk stage: 256 threads = 4 waves, one (chunk, head) per workgroup.
+// Intra-chunk stage.  256 threads = 4 waves.  The grid is persistent: each
+// workgroup walks (chunk, head) items with a stride of gridDim.x, from the
+// last chunk to the first (the blocks the chain kernel reads first are
+// written last and are the likeliest to still sit in the last-level cache),
+// and the raw inputs of its next item are loaded into registers while the
+// current item is computed.
+//
+// Elementwise layout: wave w owns 16-token sub-tile w and lane l owns the CPT
+// channels CPT*l.. (CPT = d_k/64) across all 16 tokens, so the chunk-local
+// cumsum runs inside each thread and only the four tile totals are
+// exchanged.  Log-decays are kept in log2 units (one exp2 per factor).
+//
+// Sub-tile references.  Let B_m be lam just before tile m (B_0 = 0) and
+// T_m = B_{m+1} - B_m <= 0 the tile's total.  Row operands carry
+// exp(lam_r - B_m) in [e^-80, 1]; the column operand met by row tile m
+// carries exp(B_m - lam_i): for i in tile m (diagonal pair) that lies in
+// [1, e^80] (inside the bf16 and fp32 range, the "lower-bounded decay"
+// argument of §2.1.1), for i in an earlier tile it is <= 1.  The column
+// operands of all ten (m, n) pairs are formed here, so the Gram products need
+// no rescaling.
 // -----------------------------------------------------------------------------
+template <typename T, int N> struct Vec { typedef T type __attribute__((ext_vector_type(N))); };
+
+constexpr float LOG2E = 1.4426950408889634f;
+
 template <typename T, int DK, int DV> struct IntraSmem {
     static constexpr int PR = DK + 8;     // padded row of token-major arrays
     static constexpr int PT = CHUNK + 8;  // padded row of channel-major arrays
+    static constexpr int LP = CHUNK + 4;  // fp32 row pitch of L and its inverse
+    // Column-operand rows: [0,64) exp(B_n - lam) for tile n (diagonal pairs);
+    // [64,112) exp(B_{n+1} - lam) for tiles 0..2 (pairs (n+1, n)); [112,128)
+    // tile 0 at B_2; [128,144) tile 0 at B_3; [144,160) tile 1 at B_3.
+    static constexpr int NCOL = 160;
     union {
         struct {
-            T KR[CHUNK][PR];   // k * exp(lam - lam_16m): row operand of L (tile-start reference)
-            T QR[CHUNK][PR];   // scale * q * exp(lam - lam_16m): row operand of A
-        } ops;
-        struct {
-            float Ti[CHUNK][CHUNK + 1];  // (I + L)^-1
-            T Tp[CHUNK][PT];             // (I + L)^-1 Diag(beta)
-        } inv;
+            T KR[CHUNK][PR];   // k * exp(lam - B_m): row operand of L
+            T QR[CHUNK][PR];   // scale * q * exp(lam - B_m): row operand of A
+        } ops;                 // P1 -> P2
+        float Ti[CHUNK][LP];   // (I + L)^-1 (P3)
     } x;
-    T Kc[CHUNK][PR];    // k * exp(lam_16n - lam): column operand (tile-start reference)
-    T Qp[CHUNK][PR];    // scale * q * exp(lam), staged for the fragment copy
-    T KpT[DK][PT];      // (k * exp(lam))^T, A operand of W^T
-    T KtT[DK][PT];      // (k * exp(lam_C - lam))^T, staged for the fragment copy
-    T VT[DV][PT];       // v^T, B operand of U
-    float L[CHUNK][CHUNK + 1];  // strictly lower part used; upper blocks serve as scratch
-    float F[6][DK];     // exp(lam_16m - lam_16n) for n < m, index m(m-1)/2 + n
-    float E[4][DK];     // lam at the first token of each 16-token tile
+    float L[CHUNK][LP];        // Diag(beta) StrictTril(...); upper blocks serve as scratch (P2 -> P3)
+    union {
+        T KC[NCOL][PR];    // column operands (P1 -> P2)
+        T Tp[CHUNK][PT];   // (I + L)^-1 Diag(beta) (P3 -> P4)
+    } y;
+    T KpT[DK][PT];         // (k * exp(lam))^T, A operand of W^T
+    T VT[DV][PT];          // v^T, B operand of U
+    float tot[4][DK];      // tile totals T_m (log2 units)
     float beta[CHUNK];
 };
+
+__device__ __forceinline__ int colop_row(int m, int n)
+{
+    if (m == n) return 16 * n;
+    if (m == n + 1) return 64 + 16 * n;
+    return (n == 0) ? (m == 2 ? 112 : 128) : 144;
+}
+
+// Raw inputs of one (chunk, head) in registers, unconverted (converting at
+// load time would make the wave wait for the loads): lane l of wave w holds
+// channels CPT*l.. of tokens 16w..16w+15 of g, k, q, value columns CPV*l.. of
+// the same tokens, and (lanes 0..15) beta of token 16w + l.
+template <typename T, int DK, int DV> struct RawIn {
+    static constexpr int CPT = DK / 64, CPV = DV / 64;
+    typedef typename Vec<T, CPT>::type ku;
+    typedef typename Vec<T, CPV>::type vu;
+    ku g[SUB], k[SUB], q[SUB];
+    vu v[SUB];
+    T beta;
+    float alog;
+};
+
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void load_raw(RawIn<T, DK, DV> &in, const PrefillParams &p, int tok0, int len,
+                                         int h, int w, int l)
+{
+    using R = RawIn<T, DK, DV>;
+    typedef typename R::ku ku;
+    typedef typename R::vu vu;
+    const T *gg = (const T *)p.g, *kg = (const T *)p.k, *qg = (const T *)p.q, *vg = (const T *)p.v;
+    ku zk;
+    vu zv;
+#pragma unroll
+    for (int c = 0; c < R::CPT; ++c) zk[c] = from_f<T>(0.f);
+#pragma unroll
+    for (int c = 0; c < R::CPV; ++c) zv[c] = from_f<T>(0.f);
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) {
+        const int tok = SUB * w + r;
+        const bool ok = tok < len;
+        const size_t row = (size_t)(tok0 + tok) * p.H + h;
+        in.g[r] = ok ? *reinterpret_cast<const ku *>(gg + row * DK + R::CPT * l) : zk;
+        in.k[r] = ok ? *reinterpret_cast<const ku *>(kg + row * DK + R::CPT * l) : zk;
+        in.q[r] = ok ? *reinterpret_cast<const ku *>(qg + row * DK + R::CPT * l) : zk;
+        in.v[r] = ok ? *reinterpret_cast<const vu *>(vg + row * DV + R::CPV * l) : zv;
+    }
+    const int bt = SUB * w + l;
+    in.beta = (l < SUB && bt < len) ? ((const T *)p.beta)[(size_t)(tok0 + bt) * p.H + h] : from_f<T>(0.f);
+    in.alog = p.A_log ? p.A_log[h] : 0.f;
+}
+
+// Token range of chunk c; false if c is past the last chunk (packed tail).
+__device__ __forceinline__ bool locate_chunk(const PrefillParams &p, int c, int &tok0, int &len)
+{
+    if (p.varlen) {
+        if (c >= p.chunk_off[p.N]) return false;
+        int lo = 0, hi = p.N - 1;  // largest s with chunk_off[s] <= c
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.chunk_off[mid] <= c) lo = mid; else hi = mid - 1;
+        }
+        tok0 = p.cu[lo] + (c - p.chunk_off[lo]) * CHUNK;
+        len = min(CHUNK, p.cu[lo + 1] - tok0);
+    } else {
+        const int cps = (p.T + CHUNK - 1) / CHUNK;
+        const int s = c / cps, lc = c - s * cps;
+        tok0 = s * p.T + lc * CHUNK;
+        len = min(CHUNK, p.T - lc * CHUNK);
+    }
+    return true;
+}
+
+// Next valid item at or after i (stride gridDim.x); items run chunk-major
+// from the last chunk down.  Returns false when the walk is done.
+__device__ __forceinline__ bool next_item(const PrefillParams &p, int &i, int &c, int &h, int &tok0, int &len)
+{
+    const int n_items = p.n_chunks_cap * p.H;
+    for (; i < n_items; i += gridDim.x) {
+        const int ci = i / p.H;
+        h = i - ci * p.H;
+        c = p.n_chunks_cap - 1 - ci;
+        if (locate_chunk(p, c, tok0, len)) return true;
+    }
+    return false;
+}
 
 // (m, n) sub-tile pairs (n <= m) handled by wave w in step s, as the index
 // m(m+1)/2 + n; -1 = none.  Balances the 10 pairs over 4 waves as 3/3/2/2.
@@ -172,286 +282,277 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
 {
     using BL = Block<T, DK, DV>;
     using SM = IntraSmem<T, DK, DV>;
-    constexpr int KS = DK / 32, RT = DK / 64;
+    using R = RawIn<T, DK, DV>;
+    constexpr int KS = DK / 32, RT = DK / 64, CPT = R::CPT, CPV = R::CPV;
+    typedef typename R::ku ku;
+    typedef typename Vec<T, SUB>::type tok16;
+    typedef typename Vec<T, 4>::type tok4;
     extern __shared__ __align__(16) char smem_raw[];
     SM &sm = *reinterpret_cast<SM *>(smem_raw);
 
-    const int c = blockIdx.x, h = blockIdx.y;
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, x = l & 15;
+    const int ch0 = CPT * l;  // first channel of this lane in the elementwise phase
 
-    // ---- locate the chunk ----------------------------------------------------
-    int tok0, len;
-    if (p.varlen) {
-        if (c >= p.chunk_off[p.N]) return;
-        int lo = 0, hi = p.N - 1;  // largest s with chunk_off[s] <= c
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.chunk_off[mid] <= c) lo = mid; else hi = mid - 1;
-        }
-        tok0 = p.cu[lo] + (c - p.chunk_off[lo]) * CHUNK;
-        len = min(CHUNK, p.cu[lo + 1] - tok0);
-    } else {
-        const int cps = (p.T + CHUNK - 1) / CHUNK;
-        const int s = c / cps, lc = c - s * cps;
-        tok0 = s * p.T + lc * CHUNK;
-        len = min(CHUNK, p.T - lc * CHUNK);
-    }
-    char *blkb = p.blocks + ((size_t)h * p.n_chunks_cap + c) * BL::BYTES;
-    T *blk = reinterpret_cast<T *>(blkb);
-    float *gamma_out = reinterpret_cast<float *>(blkb + BL::GAMMA_BYTE);
-    const T *qg = (const T *)p.q, *kg = (const T *)p.k, *vg = (const T *)p.v, *gg = (const T *)p.g;
-    const T *bg = (const T *)p.beta;
+    int i = blockIdx.x, c, h, tok0, len;
+    bool have = next_item(p, i, c, h, tok0, len);
+    R raw;
+    if (have) load_raw(raw, p, tok0, len, h, w, l);
 
-    // ---- P1: gate, chunk-local cumsum, elementwise operands ------------------
-    // Thread = 8 consecutive channels x TPP consecutive tokens (16-byte loads).
-    constexpr int CG8 = DK / 8, NPT = 256 / CG8, TPP = CHUNK / NPT;
-    const int cg = t % CG8, pp = t / CG8, j0 = cg * 8, r0 = pp * TPP, m0 = r0 / SUB;
-    float lam[TPP][8];
-    float lamC[8];
-    {
-        const float eA = p.A_log ? __expf(p.A_log[h]) : 0.f;
-        float run[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    while (have) {
+        char *blkb = p.blocks + ((size_t)h * p.n_chunks_cap + c) * BL::BYTES;
+        T *blk = reinterpret_cast<T *>(blkb);
+        float *gamma_out = reinterpret_cast<float *>(blkb + BL::GAMMA_BYTE);
+
+        // ---- P1: gate (eq. 5), in-tile cumsum, elementwise operands ----------
+        // The raw registers were loaded during the previous item (or before the
+        // loop); wait for them once here rather than at a conservative point
+        // behind this item's first store.
+        __builtin_amdgcn_s_waitcnt(0);
+        float lam2[SUB][CPT];  // (lam_r - B_w) log2(e) for this wave's tokens
+        {
+            const float cz = -__expf(raw.alog) * LOG2E;  // exp(-e^A z) = exp2(cz z)
+            const float gm2 = p.g_min * LOG2E;
+            float run[CPT];
 #pragma unroll
-        for (int a = 0; a < TPP; ++a) {
-            const int r = r0 + a;
-            float gv[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // tokens past the end: g = 0
-            if (r < len) {
-                const frag_t<T> raw = load8(gg + ((size_t)(tok0 + r) * p.H + h) * DK + j0);
+            for (int cc = 0; cc < CPT; ++cc) run[cc] = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float z = to_f<T>(raw[e]);
-                    gv[e] = p.A_log ? gate_from_logit(z, eA, p.g_min) : clamp_logdecay(z, p.g_min);
+            for (int r = 0; r < SUB; ++r) {
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    const float z = to_f<T>(raw.g[r][cc]);
+                    float g2 = p.A_log ? gm2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(cz * z))
+                                       : clamp_logdecay(z, p.g_min) * LOG2E;
+                    g2 = (SUB * w + r < len) ? g2 : 0.f;  // tokens past the end keep S unchanged
+                    run[cc] += g2;
+                    lam2[r][cc] = run[cc];
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { run[e] += gv[e]; lam[a][e] = run[e]; }
+            for (int cc = 0; cc < CPT; ++cc) sm.tot[w][ch0 + cc] = run[cc];
+            if (l < SUB) sm.beta[SUB * w + l] = to_f<T>(raw.beta);
         }
-        float *tot = &sm.L[0][0];  // [NPT][DK] part totals (L is free until P2)
+        lds_barrier();
+        {
+            float eBm[CPT], eCB[CPT], eT[CPT], eX1[CPT], eX2[CPT], gC[CPT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tot[pp * DK + j0 + e] = run[e];
-        __syncthreads();
-        float carry[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lamC[e] = 0.f;
-        for (int q2 = 0; q2 < NPT; ++q2) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v2 = tot[q2 * DK + j0 + e];
-                if (q2 < pp) carry[e] += v2;
-                lamC[e] += v2;
+            for (int cc = 0; cc < CPT; ++cc) {
+                const float t0 = sm.tot[0][ch0 + cc], t1 = sm.tot[1][ch0 + cc];
+                const float t2 = sm.tot[2][ch0 + cc], t3 = sm.tot[3][ch0 + cc];
+                const float Bm = (w > 0 ? t0 : 0.f) + (w > 1 ? t1 : 0.f) + (w > 2 ? t2 : 0.f);
+                const float C2 = t0 + t1 + t2 + t3;
+                eBm[cc] = __builtin_amdgcn_exp2f(Bm);              // exp(B_w)            <= 1
+                eCB[cc] = __builtin_amdgcn_exp2f(C2 - Bm);         // exp(lam_C - B_w)    <= 1
+                const float Tw = (w == 0) ? t0 : (w == 1 ? t1 : (w == 2 ? t2 : t3));
+                eT[cc] = __builtin_amdgcn_exp2f(Tw);               // exp(T_w): reference moved to the tile end
+                eX1[cc] = __builtin_amdgcn_exp2f(w == 0 ? t1 : t2);  // tile 0 -> B_2, tile 1 -> B_3
+                eX2[cc] = __builtin_amdgcn_exp2f(t1 + t2);           // tile 0 -> B_3
+                gC[cc] = __builtin_amdgcn_exp2f(C2);
             }
-        }
+            tok16 kpv[CPT], ktv[CPT];
 #pragma unroll
-        for (int a = 0; a < TPP; ++a)
+            for (int r = 0; r < SUB; ++r) {
+                const int tok = SUB * w + r;
+                ku kr_, qr_, kc_, ke_, kx1_, kx2_, qp_;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) lam[a][e] += carry[e];
-        if (r0 % SUB == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm.E[m0][j0 + e] = lam[0][e];
-        }
-        if (pp == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gamma_out[j0 + e] = __expf(lamC[e]);
-        }
-        if (t < CHUNK) sm.beta[t] = (t < len) ? to_f<T>(bg[(size_t)(tok0 + t) * p.H + h]) : 0.f;
-    }
-    __syncthreads();
-    {
-        float Em[8], eEm[8], eCm[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            Em[e] = sm.E[m0][j0 + e];
-            eEm[e] = __expf(Em[e]);             // exp(lam_16m)            (<= 1)
-            eCm[e] = __expf(lamC[e] - Em[e]);   // exp(lam_C - lam_16m)    (<= 1)
-        }
-#pragma unroll
-        for (int a = 0; a < TPP; ++a) {
-            const int r = r0 + a;
-            float kv[8] = {0, 0, 0, 0, 0, 0, 0, 0}, qv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (r < len) {
-                const size_t off = ((size_t)(tok0 + r) * p.H + h) * DK + j0;
-                const frag_t<T> kr = load8(kg + off);
-                const frag_t<T> qr = load8(qg + off);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    kv[e] = to_f<T>(kr[e]);
-                    qv[e] = p.scale * to_f<T>(qr[e]);
+                for (int cc = 0; cc < CPT; ++cc) {
+                    const float kv = to_f<T>(raw.k[r][cc]);
+                    const float qv = p.scale * to_f<T>(raw.q[r][cc]);
+                    const float eR = __builtin_amdgcn_exp2f(lam2[r][cc]);        // exp(lam_r - B_w) <= 1
+                    const float eC = __builtin_amdgcn_rcpf(eR);  // exp(B_w - lam_r) <= e^80
+                    const float kr = kv * eR, qr = qv * eR, kcs = kv * eC, kce = kcs * eT[cc];
+                    kr_[cc] = from_f<T>(kr);
+                    qr_[cc] = from_f<T>(qr);
+                    kc_[cc] = from_f<T>(kcs);
+                    ke_[cc] = from_f<T>(kce);
+                    kx1_[cc] = from_f<T>(kce * eX1[cc]);
+                    kx2_[cc] = from_f<T>(kce * eX2[cc]);
+                    qp_[cc] = from_f<T>(qr * eBm[cc]);
+                    kpv[cc][r] = from_f<T>(kr * eBm[cc]);
+                    ktv[cc][r] = from_f<T>(kcs * eCB[cc]);
+                }
+                *reinterpret_cast<ku *>(&sm.x.ops.KR[tok][ch0]) = kr_;
+                *reinterpret_cast<ku *>(&sm.x.ops.QR[tok][ch0]) = qr_;
+                *reinterpret_cast<ku *>(&sm.y.KC[tok][ch0]) = kc_;
+                if (w < 3) *reinterpret_cast<ku *>(&sm.y.KC[64 + tok][ch0]) = ke_;
+                if (w == 0) {
+                    *reinterpret_cast<ku *>(&sm.y.KC[112 + r][ch0]) = kx1_;
+                    *reinterpret_cast<ku *>(&sm.y.KC[128 + r][ch0]) = kx2_;
+                }
+                if (w == 1) *reinterpret_cast<ku *>(&sm.y.KC[144 + r][ch0]) = kx1_;
+                // Q+ as the chain's operand fragment (kmap along channels): token tok ->
+                // wave w, lane r + 16 gq, element 4 half + ch0 % 4 of k-step ch0 / 32
+                {
+                    const int cq = ch0 % 32, hq = cq / 16, gq = (cq % 16) / 4;
+                    *reinterpret_cast<ku *>(blk + BL::Q_OFF + ((w * KS + ch0 / 32) * 64 + r + 16 * gq) * 8 + 4 * hq +
+                                            cq % 4) = qp_;
                 }
             }
-            float kr_[8], qr_[8], kc_[8], qp_[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float d = lam[a][e] - Em[e];  // lam_r - lam_16m in [-75, 0]
-                const float eR = __expf(d);
-                const float eC = __expf(-d);
-                kr_[e] = kv[e] * eR;
-                qr_[e] = qv[e] * eR;
-                kc_[e] = kv[e] * eC;
-                qp_[e] = qr_[e] * eEm[e];
-                sm.KpT[j0 + e][r] = from_f<T>(kr_[e] * eEm[e]);
-                sm.KtT[j0 + e][r] = from_f<T>(kc_[e] * eCm[e]);
+            for (int cc = 0; cc < CPT; ++cc) {
+                const int ch = ch0 + cc;
+                *reinterpret_cast<tok16 *>(&sm.KpT[ch][SUB * w]) = kpv[cc];
+                // (K gamma^C / Gamma)^T fragments of the chain: rows = channels, k = tokens (kmap)
+                const int wq = ch / (16 * RT), rt = (ch / 16) % RT, xq = ch % 16, ks = w / 2, half = w % 2;
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    tok4 q4;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) q4[ii] = ktv[cc][4 * gq + ii];
+                    *reinterpret_cast<tok4 *>(blk + BL::KT_OFF + (((wq * RT + rt) * 2 + ks) * 64 + xq + 16 * gq) * 8 +
+                                              4 * half) = q4;
+                }
             }
-            store8(&sm.x.ops.KR[r][j0], make_frag<T>(kr_));
-            store8(&sm.x.ops.QR[r][j0], make_frag<T>(qr_));
-            store8(&sm.Kc[r][j0], make_frag<T>(kc_));
-            store8(&sm.Qp[r][j0], make_frag<T>(qp_));
-        }
-        // per-channel tile-pair factors
-        for (int idx = t; idx < 6 * DK; idx += 256) {
-            const int pi = idx / DK, j = idx % DK;
-            const int m = (pi == 0) ? 1 : (pi < 3 ? 2 : 3);
-            const int n = pi - m * (m - 1) / 2;
-            sm.F[pi][j] = __expf(sm.E[m][j] - sm.E[n][j]);
-        }
-        // v^T
-        constexpr int VG8 = DV / 8, VNP = 256 / VG8, VTP = CHUNK / VNP;
-        const int vc = t % VG8, vp = t / VG8;
+            if (w == 0) {  // gamma^C, stored after the last use of the raw registers
 #pragma unroll
-        for (int a = 0; a < VTP; ++a) {
-            const int r = vp * VTP + a;
-            frag_t<T> vr;
-            if (r < len) {
-                vr = load8(vg + ((size_t)(tok0 + r) * p.H + h) * DV + vc * 8);
+                for (int cc = 0; cc < CPT; ++cc) gamma_out[ch0 + cc] = gC[cc];
+            }
+#pragma unroll
+            for (int cv = 0; cv < CPV; ++cv) {
+                tok16 col;
+#pragma unroll
+                for (int r = 0; r < SUB; ++r) col[r] = raw.v[r][cv];
+                *reinterpret_cast<tok16 *>(&sm.VT[CPV * l + cv][SUB * w]) = col;
+            }
+        }
+        // prefetch the next item's raw inputs (the registers are free now)
+        int i2 = i + gridDim.x, c2 = 0, h2 = 0, tok2 = 0, len2 = 0;
+        const bool have2 = next_item(p, i2, c2, h2, tok2, len2);
+        if (have2) load_raw(raw, p, tok2, len2, h2, w, l);
+        lds_barrier();
+
+        // ---- P2: L and A sub-tiles on MFMA ----------------------------------
+        {
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                const int pi = pair_of(w, s);
+                if (pi < 0) break;
+                const int m = (pi == 0) ? 0 : (pi < 3 ? 1 : (pi < 6 ? 2 : 3));
+                const int n = pi - m * (m + 1) / 2;
+                const int cr = colop_row(m, n);
+                f32x4 aL = {0.f, 0.f, 0.f, 0.f}, aA = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const frag_t<T> kr = load_frag_lin<T>(&sm.x.ops.KR[16 * m + x][32 * ks], g);
+                    const frag_t<T> qr = load_frag_lin<T>(&sm.x.ops.QR[16 * m + x][32 * ks], g);
+                    const frag_t<T> kc = load_frag_lin<T>(&sm.y.KC[cr + x][32 * ks], g);
+                    aL = mma(kr, kc, aL);   // rows r (tile m), cols i (tile n)
+                    aA = mma(kc, qr, aA);   // rows i (tile n), cols r (tile m): A^T
+                }
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int row = 16 * m + 4 * g + ii, col = 16 * n + x;
+                    sm.L[row][col] = (col < row) ? sm.beta[row] * aL[ii] : 0.f;
+                }
+                f32x4 a4;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int r = 16 * m + x, col = 16 * n + 4 * g + ii;
+                    a4[ii] = (col <= r) ? aA[ii] : 0.f;
+                }
+                *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
+                    make_quad<T>(a4);
+            }
+            if (w >= 2) {  // the all-zero upper tiles inside used k-steps: (0,1) and (2,3)
+                const int m = (w == 2) ? 0 : 2, n = m + 1;
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
+                    make_quad<T>(z);
+            }
+        }
+        lds_barrier();  // L complete; KR / QR / KC fully read (Ti may overwrite them)
+        // ---- P3: T' = (I + L)^-1 Diag(beta), 16x16 blocks ---------------------
+        {
+            float(*L)[SM::LP] = sm.L;
+            float(*Ti)[SM::LP] = sm.x.Ti;
+            if (w == 0) {
+                // column cc of the inverse of the unit lower diagonal block mb
+                const int mb = l >> 4, cc = l & 15, o0 = 16 * mb;
+                float xv[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float acc = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+                    for (int k2 = 0; k2 < r; ++k2) acc -= L[o0 + r][o0 + k2] * xv[k2];
+                    xv[r] = acc;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Ti[o0 + r][o0 + cc] = xv[r];
             } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vr[e] = from_f<T>(0.f);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm.VT[vc * 8 + e][r] = vr[e];
-        }
-    }
-    __syncthreads();
-
-    // ---- P2: L and A tiles on MFMA; Q+ and K~^T fragments out ----------------
-    {
-        // (m, n) pairs, n <= m, balanced over the 4 waves; index m(m+1)/2 + n.
-        for (int s = 0; s < 3; ++s) {
-            const int pi = pair_of(w, s);
-            if (pi < 0) break;
-            const int m = (pi == 0) ? 0 : (pi < 3 ? 1 : (pi < 6 ? 2 : 3));
-            const int n = pi - m * (m + 1) / 2;
-            const float *Fr = (n < m) ? sm.F[m * (m - 1) / 2 + n] : nullptr;
-            f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int kb = 32 * ks + 8 * g;
-                float kr8[8], qr8[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float f = Fr ? Fr[kb + e] : 1.f;
-                    kr8[e] = to_f<T>(sm.x.ops.KR[16 * m + x][kb + e]) * f;
-                    qr8[e] = to_f<T>(sm.x.ops.QR[16 * m + x][kb + e]) * f;
+                for (int e = t - 64; e < 6 * 256; e += 192) {  // upper off-diagonal blocks are zero
+                    const int bi = e / 256, a = (e / 16) % 16, b = e % 16;
+                    const int mb = (bi < 3) ? 0 : (bi < 5 ? 1 : 2);
+                    const int nb = (bi < 3) ? bi + 1 : (bi < 5 ? bi - 1 : 3);
+                    Ti[16 * mb + a][16 * nb + b] = 0.f;
                 }
-                const frag_t<T> kc = load_frag_lin<T>(&sm.Kc[16 * n + x][32 * ks], g);
-                accL = mma(make_frag<T>(kr8), kc, accL);   // rows r (tile m), cols i (tile n)
-                accA = mma(kc, make_frag<T>(qr8), accA);   // rows i (tile n), cols r (tile m): A^T
             }
+            lds_barrier();
+            // Ti_mn = -Ti_mm sum_{q=n}^{m-1} L_mq Ti_qn, block row by block row; wave n
+            // computes block column n with fp32 MFMA (16x16x4, k = 4e + g at step e).
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * m + 4 * g + i, col = 16 * n + x;
-                sm.L[row][col] = (col < row) ? sm.beta[row] * accL[i] : 0.f;
-            }
-            f32x4 a4;
+            for (int m = 1; m < 4; ++m) {
+                if (w < m) {
+                    const int n = w;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * m + x, col = 16 * n + 4 * g + i;
-                a4[i] = (col <= r) ? accA[i] : 0.f;
+                    for (int qb = 0; qb < m; ++qb)
+                        if (qb >= n)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(L[16 * m + x][16 * qb + 4 * e + g],
+                                                                       Ti[16 * qb + 4 * e + g][16 * n + x], acc, 0, 0, 0);
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) L[16 * n + 4 * g + ii][16 * m + x] = acc[ii];  // scratch
+                }
+                lds_barrier();
+                if (w < m) {
+                    const int n = w;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ti[16 * m + x][16 * m + 4 * e + g],
+                                                                   L[16 * n + 4 * e + g][16 * m + x], acc, 0, 0, 0);
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) Ti[16 * m + 4 * g + ii][16 * n + x] = -acc[ii];
+                }
+                lds_barrier();
             }
-            *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
-                make_quad<T>(a4);
+            {
+                const int k2 = t % CHUNK, r0 = t / CHUNK;  // column k2, rows r0, r0+4, ...
+                const float bk = sm.beta[k2];
+                float tv[CHUNK / 4];
+#pragma unroll
+                for (int j = 0; j < CHUNK / 4; ++j) tv[j] = Ti[r0 + 4 * j][k2];
+#pragma unroll
+                for (int j = 0; j < CHUNK / 4; ++j) sm.y.Tp[r0 + 4 * j][k2] = from_f<T>(tv[j] * bk);
+            }
         }
-        if (w >= 2) {  // the two all-zero upper tiles of A inside used k-steps: (0,1) and (2,3)
-            const int m = (w == 2) ? 0 : 2, n = m + 1;
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
-                make_quad<T>(z);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            store8(blk + BL::Q_OFF + ((w * KS + ks) * 64 + l) * 8, load_frag_kmap<T>(&sm.Qp[16 * w + x][32 * ks], g));
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                store8(blk + BL::KT_OFF + (((w * RT + rt) * 2 + ks) * 64 + l) * 8,
-                       load_frag_kmap<T>(&sm.KtT[16 * (w * RT + rt) + x][32 * ks], g));
-    }
-    __syncthreads();
+        lds_barrier();
 
-    // ---- P3: T' = (I + L)^-1 Diag(beta), blocked, fp32 ------------------------
-    {
-        float(*Ti)[CHUNK + 1] = sm.x.inv.Ti;
-        if (t < 64) {
-            // column cc of the inverse of the unit lower 16x16 diagonal block mb
-            const int mb = t >> 4, cc = t & 15, o0 = 16 * mb;
-            float xv[16];
+        // ---- P4: U = T' V and W^T = K+^T T'^T on MFMA -------------------------
+        for (int ct = w; ct < DV / 16; ct += 4) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == cc) ? 1.f : 0.f;
-#pragma unroll
-                for (int i = 0; i < r; ++i) acc -= sm.L[o0 + r][o0 + i] * xv[i];
-                xv[r] = acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Ti[o0 + r][o0 + cc] = xv[r];
-        } else {
-            for (int e = t - 64; e < 6 * 256; e += 192) {  // upper off-diagonal blocks are zero
-                const int bi = e / 256, a = (e / 16) % 16, b = e % 16;
-                const int mb = (bi < 3) ? 0 : (bi < 5 ? 1 : 2);
-                const int nb = (bi < 3) ? bi + 1 : (bi < 5 ? bi - 1 : 3);
-                Ti[16 * mb + a][16 * nb + b] = 0.f;
+            for (int m = 0; m < 4; ++m) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks <= m / 2; ++ks)
+                    acc = mma(load_frag_lin<T>(&sm.y.Tp[16 * m + x][32 * ks], g),
+                              load_frag_lin<T>(&sm.VT[16 * ct + x][32 * ks], g), acc);
+                *reinterpret_cast<quad_t<T> *>(blk + BL::U_OFF + ((ct * 4 + m) * 64 + l) * 4) = make_quad<T>(acc);
             }
         }
-        __syncthreads();
-        for (int m = 1; m < 4; ++m) {
-            // X_n = sum_{p=n}^{m-1} L_mp Ti_pn, parked in the unused upper block (n, m) of L
-            for (int e = t; e < m * 256; e += 256) {
-                const int n = e / 256, a = (e / 16) % 16, b = e % 16;
-                float acc = 0.f;
-                for (int pb = n; pb < m; ++pb)
+        for (int ct = w; ct < DK / 16; ct += 4) {
 #pragma unroll
-                    for (int cc = 0; cc < 16; ++cc)
-                        acc += sm.L[16 * m + a][16 * pb + cc] * Ti[16 * pb + cc][16 * n + b];
-                sm.L[16 * n + a][16 * m + b] = acc;
+            for (int tt = 0; tt < 4; ++tt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks <= tt / 2; ++ks)
+                    acc = mma(load_frag_lin<T>(&sm.KpT[16 * ct + x][32 * ks], g),
+                              load_frag_lin<T>(&sm.y.Tp[16 * tt + x][32 * ks], g), acc);
+                *reinterpret_cast<quad_t<T> *>(blk + BL::W_OFF + ((tt * KS + ct / 2) * 64 + l) * 8 + 4 * (ct % 2)) =
+                    make_quad<T>(-acc);
             }
-            __syncthreads();
-            for (int e = t; e < m * 256; e += 256) {
-                const int n = e / 256, a = (e / 16) % 16, b = e % 16;
-                float acc = 0.f;
-#pragma unroll
-                for (int cc = 0; cc < 16; ++cc) acc += Ti[16 * m + a][16 * m + cc] * sm.L[16 * n + cc][16 * m + b];
-                Ti[16 * m + a][16 * n + b] = -acc;
-            }
-            __syncthreads();
         }
-        for (int e = t; e < CHUNK * CHUNK; e += 256) {
-            const int r = e / CHUNK, i = e % CHUNK;
-            sm.x.inv.Tp[r][i] = from_f<T>(Ti[r][i] * sm.beta[i]);
-        }
-    }
-    __syncthreads();
-
-    // ---- P4: U = T' V and W^T = K+^T T'^T on MFMA ----------------------------
-    for (int ct = w; ct < DV / 16; ct += 4) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int ks = 0; ks <= m / 2; ++ks)
-                acc = mma(load_frag_lin<T>(&sm.x.inv.Tp[16 * m + x][32 * ks], g),
-                          load_frag_lin<T>(&sm.VT[16 * ct + x][32 * ks], g), acc);
-            *reinterpret_cast<quad_t<T> *>(blk + BL::U_OFF + ((ct * 4 + m) * 64 + l) * 4) = make_quad<T>(acc);
-        }
-    }
-    for (int ct = w; ct < DK / 16; ct += 4) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int ks = 0; ks <= tt / 2; ++ks)
-                acc = mma(load_frag_lin<T>(&sm.KpT[16 * ct + x][32 * ks], g),
-                          load_frag_lin<T>(&sm.x.inv.Tp[16 * tt + x][32 * ks], g), acc);
-            *reinterpret_cast<quad_t<T> *>(blk + BL::W_OFF + ((tt * KS + ct / 2) * 64 + l) * 8 + 4 * (ct % 2)) =
-                make_quad<T>(-acc);
-        }
+        lds_barrier();  // LDS is reused by the next item
+        i = i2; c = c2; h = h2; tok0 = tok2; len = len2;
+        have = have2;
     }
 }
 
@@ -459,16 +560,51 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
 // Chain stage: one workgroup (4 waves) per (sequence, head, 16-column slice).
 // Workgroup ids are dispatched round-robin over the 8 XCDs (id % 8), so the NS
 // slices of one (sequence, head) are given ids congruent mod 8: they share an
-// XCD and read the chunk blocks through one L2.
+// XCD and read the chunk blocks through one L2.  The operand fragments of the
+// next two chunks are in flight while the current chunk is computed.
 // -----------------------------------------------------------------------------
+template <typename T, int DK> struct ChainFrags {
+    static constexpr int KS = DK / 32, RT = DK / 64;
+    frag_t<T> Wn[KS], Qp[KS], Af[2], Kt[RT][2];
+    quad_t<T> U;
+    f32x4 gam[RT];
+};
+
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void load_chain(ChainFrags<T, DK> &f, const char *blkb, int w, int l, int g, int sl)
+{
+    using BL = Block<T, DK, DV>;
+    constexpr int KS = DK / 32, RT = DK / 64;
+    const T *blk = reinterpret_cast<const T *>(blkb);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        f.Wn[ks] = load8(blk + BL::W_OFF + ((w * KS + ks) * 64 + l) * 8);
+        f.Qp[ks] = load8(blk + BL::Q_OFF + ((w * KS + ks) * 64 + l) * 8);
+    }
+    f.Af[0] = load8(blk + BL::A_OFF + ((w * 2) * 64 + l) * 8);
+    if (w >= 2) f.Af[1] = load8(blk + BL::A_OFF + ((w * 2 + 1) * 64 + l) * 8);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            f.Kt[rt][ks] = load8(blk + BL::KT_OFF + (((w * RT + rt) * 2 + ks) * 64 + l) * 8);
+    f.U = *reinterpret_cast<const quad_t<T> *>(blk + BL::U_OFF + ((sl * 4 + w) * 64 + l) * 4);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+        f.gam[rt] = *reinterpret_cast<const f32x4 *>(blkb + BL::GAMMA_BYTE + (16 * (w * RT + rt) + 4 * g) * sizeof(float));
+}
+
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p)
 {
     using BL = Block<T, DK, DV>;
     constexpr int KS = DK / 32, RT = DK / 64, NS = DV / 16;
     constexpr int PS = DK + 8, PV = CHUNK + 8;
-    __shared__ __align__(16) T sST[16][PS];  // S^T slice: [column][state row]
-    __shared__ __align__(16) T sVT[16][PV];  // V~^T slice: [column][token]
+    // S^T and V~^T slices, [column][k], with k stored in kmap order inside each
+    // block of 32 (position 8g + e holds k = kmap(g, e)), so an operand fragment
+    // is one contiguous 16-byte read and an accumulator quad one 8-byte write.
+    __shared__ __align__(16) T sST[16][PS];
+    __shared__ __align__(16) T sVT[16][PV];
 
     const int npairs = p.N * p.H;
     const int bid = blockIdx.x, xcd = bid & 7, jj = bid >> 3;
@@ -502,61 +638,57 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p)
             const int row = 16 * (w * RT + rt) + 4 * g + i;
             S[rt][i] = p.h0 ? p.h0[sbase + (size_t)row * DV + col] : 0.f;
         }
-        *reinterpret_cast<quad_t<T> *>(&sST[x][16 * (w * RT + rt) + 4 * g]) = make_quad<T>(S[rt]);
+        *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
     }
 
+    const char *blk0 = p.blocks + ((size_t)h * p.n_chunks_cap + chunk0) * BL::BYTES;
     T *o = (T *)p.o;
-    for (int lc = 0; lc < nch; ++lc) {
-        const char *blkb = p.blocks + ((size_t)h * p.n_chunks_cap + chunk0 + lc) * BL::BYTES;
-        const T *blk = reinterpret_cast<const T *>(blkb);
-        frag_t<T> Wn[KS], Qp[KS], Af[2], Kt[RT][2];
+    // One chunk of the recurrence with operands f (already in registers).
+    auto step = [&](const ChainFrags<T, DK> &f, int lc) {
+        lds_barrier();  // S^T of this chunk's entering state is in LDS
+        frag_t<T> Sk[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            Wn[ks] = load8(blk + BL::W_OFF + ((w * KS + ks) * 64 + l) * 8);
-            Qp[ks] = load8(blk + BL::Q_OFF + ((w * KS + ks) * 64 + l) * 8);
-        }
-        Af[0] = load8(blk + BL::A_OFF + ((w * 2) * 64 + l) * 8);
-        if (w >= 2) Af[1] = load8(blk + BL::A_OFF + ((w * 2 + 1) * 64 + l) * 8);
+        for (int ks = 0; ks < KS; ++ks) Sk[ks] = load_frag_lin<T>(&sST[x][32 * ks], g);
+        f32x4 accV = quad_to_f<T>(f.U), accO = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int ks = 0; ks < KS; ++ks) accV = mma(f.Wn[ks], Sk[ks], accV);  // V~ = U - W S
+        // The output is formed transposed, O^T = S^T (Gamma Q)^T + V~^T A^T: the same
+        // fragments with the operand roles swapped, so each lane ends with four
+        // consecutive columns of one token (one 8-byte store).
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                Kt[rt][ks] = load8(blk + BL::KT_OFF + (((w * RT + rt) * 2 + ks) * 64 + l) * 8);
-        const quad_t<T> Uq = *reinterpret_cast<const quad_t<T> *>(blk + BL::U_OFF + ((sl * 4 + w) * 64 + l) * 4);
-        f32x4 gam[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            gam[rt] = *reinterpret_cast<const f32x4 *>(blkb + BL::GAMMA_BYTE +
-                                                       (16 * (w * RT + rt) + 4 * g) * sizeof(float));
-        __syncthreads();  // S^T of this chunk's entering state is in LDS
-        frag_t<T> Sf[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) Sf[ks] = load_frag_kmap<T>(&sST[x][32 * ks], g);
-        f32x4 accV = quad_to_f<T>(Uq), accO = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) accV = mma(Wn[ks], Sf[ks], accV);  // V~ = U - W S
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) accO = mma(Qp[ks], Sf[ks], accO);  // (Gamma Q) S
-        *reinterpret_cast<quad_t<T> *>(&sVT[x][16 * w + 4 * g]) = make_quad<T>(accV);
-        __syncthreads();  // V~ of the whole chunk is in LDS
+        for (int ks = 0; ks < KS; ++ks) accO = mma(Sk[ks], f.Qp[ks], accO);
+        *reinterpret_cast<quad_t<T> *>(&sVT[x][kpos(16 * w + 4 * g)]) = make_quad<T>(accV);
+        lds_barrier();  // V~ of the whole chunk is in LDS
         frag_t<T> Vf[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) Vf[ks] = load_frag_kmap<T>(&sVT[x][32 * ks], g);
-        accO = mma(Af[0], Vf[0], accO);             // + A V~ (causal: k-step 1 only for waves 2, 3)
-        if (w >= 2) accO = mma(Af[1], Vf[1], accO);
-        const int clen = min(CHUNK, len - lc * CHUNK), ctok = tok0 + lc * CHUNK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * g + i;
-            if (r < clen) o[((size_t)(ctok + r) * p.H + h) * DV + col] = from_f<T>(accO[i]);
-        }
+        for (int ks = 0; ks < 2; ++ks) Vf[ks] = load_frag_lin<T>(&sVT[x][32 * ks], g);
+        accO = mma(Vf[0], f.Af[0], accO);             // + (A V~)^T (k-step 1 only for waves 2, 3)
+        if (w >= 2) accO = mma(Vf[1], f.Af[1], accO);
+        const int clen = min(CHUNK, len - lc * CHUNK), r = 16 * w + x;
+        if (r < clen)
+            *reinterpret_cast<quad_t<T> *>(o + ((size_t)(tok0 + lc * CHUNK + r) * p.H + h) * DV + 16 * sl + 4 * g) =
+                make_quad<T>(accO);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            S[rt] *= gam[rt];                       // Diag(gamma^C) S
-            S[rt] = mma(Kt[rt][0], Vf[0], S[rt]);   // + (K gamma^C / Gamma)^T V~
-            S[rt] = mma(Kt[rt][1], Vf[1], S[rt]);
-            *reinterpret_cast<quad_t<T> *>(&sST[x][16 * (w * RT + rt) + 4 * g]) = make_quad<T>(S[rt]);
+            S[rt] *= f.gam[rt];                       // Diag(gamma^C) S
+            S[rt] = mma(f.Kt[rt][0], Vf[0], S[rt]);   // + (K gamma^C / Gamma)^T V~
+            S[rt] = mma(f.Kt[rt][1], Vf[1], S[rt]);
+            *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
         }
+    };
+    // Two operand buffers alternate: the loads of chunk lc+1 are in flight while
+    // chunk lc is computed.  Prefetches are unconditional (the chunk index is
+    // clamped; a repeated load is harmless) so the loop body stays straight-line.
+    auto fetch = [&](ChainFrags<T, DK> &f, int lc) {
+        load_chain<T, DK, DV>(f, blk0 + (size_t)min(lc, nch - 1) * BL::BYTES, w, l, g, sl);
+    };
+    ChainFrags<T, DK> fa, fb;
+    if (nch > 0) fetch(fa, 0);
+    for (int lc = 0; lc < nch; lc += 2) {
+        fetch(fb, lc + 1);
+        step(fa, lc);
+        fetch(fa, lc + 2);
+        if (lc + 1 < nch) step(fb, lc + 1);
     }
     if (p.hT) {
 #pragma unroll
@@ -570,6 +702,20 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p)
 }
 
 // -----------------------------------------------------------------------------
+// Persistent grid of the intra-chunk stage: one workgroup per compute unit
+// (its LDS footprint allows one), queried once from the device.
+static long intra_grid()
+{
+    static const long n = [] {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        return (long)cus;
+    }();
+    return n;
+}
+
 template <typename T, int DK, int DV>
 static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
 {
@@ -580,7 +726,9 @@ static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
         static const hipError_t attr = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV>,
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV>), dim3(p.n_chunks_cap, p.H), dim3(256), smem, st, p);
+        const long items = (long)p.n_chunks_cap * p.H;
+        const unsigned grid = (unsigned)(items < intra_grid() ? items : intra_grid());
+        hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV>), dim3(grid), dim3(256), smem, st, p);
     }
     const long npairs = (long)p.N * p.H;
     const unsigned grid = (unsigned)(((npairs + 7) / 8) * 8 * (DV / 16));
