@@ -19,6 +19,7 @@ Timing uses HIP events recorded on the stream the kernels run on.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -46,6 +47,27 @@ def prefill_counts(T, H, Dk, Dv, N, C=64, elem=2):
 
 def decode_counts(N, H, Dk, Dv, elem=2):
     return N * H * (2 * Dk * Dv * 4 + elem * (3 * Dk + 2 * Dv) + elem), N * H * 7 * Dk * Dv
+
+
+def profiled_traffic(name):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (copy-calibrated), read from profiles/hbm_traffic_pmc.txt.  Returns None
+    when the kernel sources no longer hash to the digest that was profiled."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if not line.startswith("record "):
+            continue
+        fields = dict(kv.split("=", 1) for kv in line.split()[1:])
+        if fields.get("name") != name:
+            continue
+        h = hashlib.sha256()
+        for f in fields["files"].split(","):
+            with open(os.path.join(ROOT, "gated_delta_rule_20_amd", "csrc", f), "rb") as fh:
+                h.update(fh.read())
+        return int(fields["traffic_bytes"]) if h.hexdigest()[:16] == fields["digest"] else None
+    return None
 
 
 def time_calls(fn, n, stream):
@@ -204,7 +226,7 @@ def main():
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd (intra_chunk_kernel + chain_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic("prefill"),
                      "algorithmic_bytes": pf["bytes"]},
         "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops": pf["flops"]},
@@ -221,7 +243,7 @@ def main():
             "tokens_per_s": dc["N"] / (dc["us"] / 1e6),
             "roofline": {"bound": "hbm", "kernel": "recurrent_step_kernel", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": None, "algorithmic_bytes": dc["bytes"]},
+                         "traffic": profiled_traffic("decode"), "algorithmic_bytes": dc["bytes"]},
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pf["inputs"])

@@ -161,7 +161,8 @@ kda_status_t kda_recurrent_step(const kda_step_args_t *a, void *stream)
     kda_status_t st = check_common(a->dtype, a->Dk, a->Dv, a->A_log, a->g_min);
     if (st != KDA_SUCCESS) return st;
     if (a->N < 0 || a->H < 1) return fail(KDA_ERROR_INVALID_VALUE, "need N >= 0, H >= 1 (got N=%d H=%d)", a->N, a->H);
-    if ((long long)a->N * a->H > 0x7fffffffLL) return fail(KDA_ERROR_NOT_SUPPORTED, "N*H too large");
+    // two workgroups per (sequence, head) must fit the launch grid
+    if ((long long)a->N * a->H > 0x3fffffffLL) return fail(KDA_ERROR_NOT_SUPPORTED, "N*H too large");
     if (a->N == 0) { g_err[0] = 0; return KDA_SUCCESS; }
     const void *req[] = {a->q, a->k, a->v, a->g, a->beta, a->state, a->o};
     const char *nm[] = {"q", "k", "v", "g", "beta", "state", "o"};

@@ -13,11 +13,14 @@
 // so one pass over S yields both reductions, and the update is applied while
 // the rows are still in registers.
 //
-// Launch: one 256-thread workgroup per (sequence, head).  Thread t owns the
-// 4 columns 4*(t % CG) .. +3 (CG = Dv / 4 column groups) and rows
+// Launch: two 256-thread workgroups per (sequence, head), each owning half of
+// the d_v columns (columns evolve independently; twice the workgroups balance
+// the 1 GiB stream better over the compute units).  Thread t owns the 4
+// columns c0 + 4*(t % CG) .. +3 (CG = column groups of the half) and rows
 // (t / CG) + RG*i (RG = 256 / CG row groups), so each load instruction of a
-// wave covers whole 512-byte rows of the state (fully coalesced 16-byte
-// accesses).  The two column reductions go through LDS once.
+// wave covers whole rows of the half (coalesced 16-byte accesses).  The two
+// column reductions go through LDS once.  The state is read and written with
+// non-temporal hints: it is streamed once per step and never re-read soon.
 #include "kda_common.h"
 
 namespace kda {
@@ -28,19 +31,21 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const T *__restrict__ gz, const T *__restrict__ beta, const float *__restrict__ A_log,
     float g_min, float scale, int H, float *__restrict__ state, T *__restrict__ o)
 {
-    constexpr int CG = DV / 4;          // column groups of 4
+    constexpr int WC = DV / 2;          // columns handled by this workgroup
+    constexpr int CG = WC / 4;          // column groups of 4
     constexpr int RG = 256 / CG;        // row groups
     constexpr int RPT = DK / RG;        // rows per thread
     static_assert(RPT * RG == DK, "row split");
 
     __shared__ float s_k[DK], s_q[DK], s_a[DK];
-    __shared__ float s_red[2][RG][DV];
-    __shared__ float s_delta[DV];
+    __shared__ float s_red[2][RG][WC];
+    __shared__ float s_delta[WC];
     __shared__ float s_kq;
 
     const int t = threadIdx.x;
     const int cg = t % CG, rg = t / CG;
-    const size_t nh = blockIdx.x;                 // sequence * H + head
+    const size_t nh = blockIdx.x / 2;             // sequence * H + head
+    const int c0 = (blockIdx.x % 2) * WC;         // first column of this half
     const int h = (int)(nh % H);
     float *S = state + nh * (size_t)(DK * DV);
 
@@ -48,7 +53,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     f32x4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-        s[i] = *reinterpret_cast<const f32x4 *>(S + (size_t)(rg + RG * i) * DV + 4 * cg);
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)(rg + RG * i) * DV + c0 + 4 * cg));
 
     if (t < DK) {
         const size_t off = nh * DK + t;
@@ -82,14 +87,14 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     *reinterpret_cast<f32x4 *>(&s_red[1][rg][4 * cg]) = r;
     __syncthreads();
 
-    if (t < DV) {
+    if (t < WC) {
         float pc = 0.f, rc = 0.f;
 #pragma unroll
         for (int x = 0; x < RG; ++x) { pc += s_red[0][x][t]; rc += s_red[1][x][t]; }
         const float b = to_f<T>(beta[nh]);
-        const float d = b * (to_f<T>(v[nh * DV + t]) - pc);
+        const float d = b * (to_f<T>(v[nh * DV + c0 + t]) - pc);
         s_delta[t] = d;
-        o[nh * DV + t] = from_f<T>(scale * (rc + d * s_kq));
+        o[nh * DV + c0 + t] = from_f<T>(scale * (rc + d * s_kq));
     }
     __syncthreads();
 
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int j = rg + RG * i;
-        *reinterpret_cast<f32x4 *>(S + (size_t)j * DV + 4 * cg) = s[i] + s_k[j] * d4;
+        __builtin_nontemporal_store(s[i] + s_k[j] * d4, reinterpret_cast<f32x4 *>(S + (size_t)j * DV + c0 + 4 * cg));
     }
 }
 
@@ -106,7 +111,7 @@ hipError_t launch_step_t(int N, int H, const void *q, const void *k, const void 
                          const void *beta, const float *A_log, float g_min, float scale,
                          float *state, void *o, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)((size_t)N * H);
+    const unsigned grid = (unsigned)((size_t)N * H * 2);
     hipLaunchKernelGGL((recurrent_step_kernel<T, DK, DV>), dim3(grid), dim3(256), 0, stream,
                        (const T *)q, (const T *)k, (const T *)v, (const T *)g, (const T *)beta,
                        A_log, g_min, scale, H, state, (T *)o);

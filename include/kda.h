@@ -113,7 +113,10 @@ KDA_API kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *args, void *strea
  * One decode step for N independent sequences (one token each), eq. (1):
  *   q, k, g : [N, H, Dk]    v, o : [N, H, Dv]    beta : [N, H]
  *   state   : [N, H, Dk, Dv] float32, read and overwritten IN PLACE with S_t.
- * Dk, Dv in {64, 128}; A_log / g as for kda_chunk_fwd.
+ * Dk, Dv in {64, 128}; A_log / g as for kda_chunk_fwd.  N = 0 is a no-op;
+ * N*H above 2^30 - 1 returns KDA_ERROR_NOT_SUPPORTED.  The state must not
+ * alias q/k/v/g/beta/o.  All pointers are device memory owned by the caller;
+ * the call allocates nothing and is asynchronous on `stream`.
  */
 typedef struct {
     int32_t N, H, Dk, Dv;

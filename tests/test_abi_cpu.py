@@ -154,3 +154,13 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.replace("oracle/", ""), f
+
+
+def test_bench_traffic_records_parse():
+    """bench.py's profiled-traffic lookup returns an int (digest matches) or
+    None (kernel changed since profiling) and never raises."""
+    import bench
+    for name in ("prefill", "decode"):
+        t = bench.profiled_traffic(name)
+        assert t is None or (isinstance(t, int) and t > 0)
+    assert bench.profiled_traffic("no-such-kernel") is None
