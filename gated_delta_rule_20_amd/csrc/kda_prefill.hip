@@ -570,29 +570,58 @@ template <typename T, int DK> struct ChainFrags {
     f32x4 gam[RT];
 };
 
-template <typename T, int DK, int DV>
-__device__ __forceinline__ void load_chain(ChainFrags<T, DK> &f, const char *blkb, int w, int l, int g, int sl)
+// Fragment with every bit ANDed with m (m = 0 or ~0): a branch-free zeroing.
+template <typename T> __device__ __forceinline__ frag_t<T> mask_frag(frag_t<T> f, uint32_t m)
 {
-    using BL = Block<T, DK, DV>;
-    constexpr int KS = DK / 32, RT = DK / 64;
-    const T *blk = reinterpret_cast<const T *>(blkb);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        f.Wn[ks] = load8(blk + BL::W_OFF + ((w * KS + ks) * 64 + l) * 8);
-        f.Qp[ks] = load8(blk + BL::Q_OFF + ((w * KS + ks) * 64 + l) * 8);
-    }
-    f.Af[0] = load8(blk + BL::A_OFF + ((w * 2) * 64 + l) * 8);
-    if (w >= 2) f.Af[1] = load8(blk + BL::A_OFF + ((w * 2 + 1) * 64 + l) * 8);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            f.Kt[rt][ks] = load8(blk + BL::KT_OFF + (((w * RT + rt) * 2 + ks) * 64 + l) * 8);
-    f.U = *reinterpret_cast<const quad_t<T> *>(blk + BL::U_OFF + ((sl * 4 + w) * 64 + l) * 4);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-        f.gam[rt] = *reinterpret_cast<const f32x4 *>(blkb + BL::GAMMA_BYTE + (16 * (w * RT + rt) + 4 * g) * sizeof(float));
+    typedef uint32_t u32v __attribute__((ext_vector_type(sizeof(frag_t<T>) / 4)));
+    u32v u = __builtin_bit_cast(u32v, f);
+    u &= m;
+    return __builtin_bit_cast(frag_t<T>, u);
 }
+
+// Loads of one chunk's operands for wave wv, in four parts so that they can be
+// spread over the previous chunk's computation.  `b` is the block (uniform);
+// each access is scalar base + lane offset + immediate.
+template <typename V> __device__ __forceinline__ V ldg(const char *b, size_t off, uint32_t lane_off)
+{
+    return *reinterpret_cast<const V *>(b + off + lane_off);
+}
+
+template <typename T, int DK, int DV> struct ChainLoad {
+    using BL = Block<T, DK, DV>;
+    static constexpr int KS = DK / 32, RT = DK / 64;
+    static constexpr size_t FB = sizeof(frag_t<T>), QB = sizeof(quad_t<T>);
+    __device__ static __forceinline__ void w(ChainFrags<T, DK> &f, const char *b, int wv, int l, int sl) {
+        f.U = ldg<quad_t<T>>(b, BL::U_OFF * sizeof(T) + (size_t)(sl * 4 + wv) * 64 * QB, (uint32_t)l * QB);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            f.Wn[ks] = ldg<frag_t<T>>(b, BL::W_OFF * sizeof(T) + (size_t)(wv * KS + ks) * 64 * FB, (uint32_t)l * FB);
+    }
+    __device__ static __forceinline__ void q(ChainFrags<T, DK> &f, const char *b, int wv, int l) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            f.Qp[ks] = ldg<frag_t<T>>(b, BL::Q_OFF * sizeof(T) + (size_t)(wv * KS + ks) * 64 * FB, (uint32_t)l * FB);
+    }
+    __device__ static __forceinline__ void a(ChainFrags<T, DK> &f, const char *b, int wv, int l) {
+        // Waves 0, 1 have no second k-step of A (all zero, not stored): they load
+        // the first one again and the step masks it to zero.
+        f.Af[0] = ldg<frag_t<T>>(b, BL::A_OFF * sizeof(T) + (size_t)(wv * 2) * 64 * FB, (uint32_t)l * FB);
+        f.Af[1] = ldg<frag_t<T>>(b, BL::A_OFF * sizeof(T) + (size_t)(wv * 2 + (wv >= 2)) * 64 * FB, (uint32_t)l * FB);
+    }
+    __device__ static __forceinline__ void kt(ChainFrags<T, DK> &f, const char *b, int wv, int l, int g) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                f.Kt[rt][ks] = ldg<frag_t<T>>(b, BL::KT_OFF * sizeof(T) + (size_t)((wv * RT + rt) * 2 + ks) * 64 * FB,
+                                              (uint32_t)l * FB);
+            f.gam[rt] = ldg<f32x4>(b, BL::GAMMA_BYTE + (size_t)(wv * RT + rt) * 64, (uint32_t)g * 16u);
+        }
+    }
+    __device__ static __forceinline__ void all(ChainFrags<T, DK> &f, const char *b, int wv, int l, int g, int sl) {
+        w(f, b, wv, l, sl); q(f, b, wv, l); a(f, b, wv, l); kt(f, b, wv, l, g);
+    }
+};
 
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p)
@@ -625,8 +654,9 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p)
         nch = (p.T + CHUNK - 1) / CHUNK;
         chunk0 = s * nch;
     }
-    const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, x = l & 15;
+    const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 4, x = l & 15;
     const int col = 16 * sl + x;
+    const uint32_t amask = (w >= 2) ? ~0u : 0u;
 
     // state slice in accumulator layout: rows 16*(w*RT+rt) + 4g + i, column col
     f32x4 S[RT];
@@ -643,8 +673,12 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p)
 
     const char *blk0 = p.blocks + ((size_t)h * p.n_chunks_cap + chunk0) * BL::BYTES;
     T *o = (T *)p.o;
-    // One chunk of the recurrence with operands f (already in registers).
-    auto step = [&](const ChainFrags<T, DK> &f, int lc) {
+    using LD = ChainLoad<T, DK, DV>;
+    // One chunk of the recurrence with operands f (already in registers); the
+    // operands of chunk nlc are loaded into nx in four parts placed between
+    // the MFMA groups, so that the wave does not stall on one burst of loads.
+    auto step = [&](const ChainFrags<T, DK> &f, int lc, ChainFrags<T, DK> &nx, int nlc) {
+        const char *nb = blk0 + (size_t)min(nlc, nch - 1) * BL::BYTES;  // last block again at the end
         lds_barrier();  // S^T of this chunk's entering state is in LDS
         frag_t<T> Sk[KS];
 #pragma unroll
@@ -652,43 +686,62 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p)
         f32x4 accV = quad_to_f<T>(f.U), accO = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) accV = mma(f.Wn[ks], Sk[ks], accV);  // V~ = U - W S
+        __builtin_amdgcn_sched_barrier(0);
+        LD::w(nx, nb, w, l, sl);
+        __builtin_amdgcn_sched_barrier(0);
         // The output is formed transposed, O^T = S^T (Gamma Q)^T + V~^T A^T: the same
         // fragments with the operand roles swapped, so each lane ends with four
         // consecutive columns of one token (one 8-byte store).
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) accO = mma(Sk[ks], f.Qp[ks], accO);
         *reinterpret_cast<quad_t<T> *>(&sVT[x][kpos(16 * w + 4 * g)]) = make_quad<T>(accV);
+        __builtin_amdgcn_sched_barrier(0);
+        LD::q(nx, nb, w, l);
+        __builtin_amdgcn_sched_barrier(0);
         lds_barrier();  // V~ of the whole chunk is in LDS
         frag_t<T> Vf[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) Vf[ks] = load_frag_lin<T>(&sVT[x][32 * ks], g);
-        accO = mma(Vf[0], f.Af[0], accO);             // + (A V~)^T (k-step 1 only for waves 2, 3)
-        if (w >= 2) accO = mma(Vf[1], f.Af[1], accO);
-        const int clen = min(CHUNK, len - lc * CHUNK), r = 16 * w + x;
-        if (r < clen)
-            *reinterpret_cast<quad_t<T> *>(o + ((size_t)(tok0 + lc * CHUNK + r) * p.H + h) * DV + 16 * sl + 4 * g) =
-                make_quad<T>(accO);
+        accO = mma(Vf[0], f.Af[0], accO);             // + (A V~)^T
+        accO = mma(Vf[1], mask_frag<T>(f.Af[1], amask), accO);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             S[rt] *= f.gam[rt];                       // Diag(gamma^C) S
             S[rt] = mma(f.Kt[rt][0], Vf[0], S[rt]);   // + (K gamma^C / Gamma)^T V~
             S[rt] = mma(f.Kt[rt][1], Vf[1], S[rt]);
-            *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        LD::a(nx, nb, w, l);
+        LD::kt(nx, nb, w, l, g);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
+        const int clen = min(CHUNK, len - lc * CHUNK), r = 16 * w + x;
+        if (r < clen)
+            *reinterpret_cast<quad_t<T> *>(o + ((size_t)(tok0 + lc * CHUNK + r) * p.H + h) * DV + 16 * sl + 4 * g) =
+                make_quad<T>(accO);
     };
-    // Two operand buffers alternate: the loads of chunk lc+1 are in flight while
-    // chunk lc is computed.  Prefetches are unconditional (the chunk index is
-    // clamped; a repeated load is harmless) so the loop body stays straight-line.
-    auto fetch = [&](ChainFrags<T, DK> &f, int lc) {
-        load_chain<T, DK, DV>(f, blk0 + (size_t)min(lc, nch - 1) * BL::BYTES, w, l, g, sl);
-    };
+    // Two operand buffers alternate (chunk indices past the end are clamped: a
+    // repeated load is harmless).  The first one or two chunks are peeled so
+    // that the loop body holds exactly two steps with no branch between them
+    // (which keeps the compiler's load waits one chunk deep).
     ChainFrags<T, DK> fa, fb;
-    if (nch > 0) fetch(fa, 0);
-    for (int lc = 0; lc < nch; lc += 2) {
-        fetch(fb, lc + 1);
-        step(fa, lc);
-        fetch(fa, lc + 2);
-        if (lc + 1 < nch) step(fb, lc + 1);
+    if (nch > 0) {
+        LD::all(fa, blk0, w, l, g, sl);
+        step(fa, 0, fb, 1);
+        if (nch & 1) {
+            for (int lc = 1; lc < nch; lc += 2) {
+                step(fb, lc, fa, lc + 1);
+                step(fa, lc + 1, fb, lc + 2);
+            }
+        } else {
+            step(fb, 1, fa, 2);
+            for (int lc = 2; lc < nch; lc += 2) {
+                step(fa, lc, fb, lc + 1);
+                step(fb, lc + 1, fa, lc + 2);
+            }
+        }
     }
     if (p.hT) {
 #pragma unroll
