@@ -461,12 +461,19 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
         }
         lds_barrier();  // L complete; KR / QR / KC fully read (Ti may overwrite them)
         // ---- P3: T' = (I + L)^-1 Diag(beta), 16x16 blocks ---------------------
+        // Diagonal blocks D_m = (I + L_mm)^-1 by substitution (wave 0, one lane
+        // per (block, column)); then wave n < 3 walks block column n downwards,
+        //   T_mn = -D_m sum_{q=n}^{m-1} L_mq T_qn,   T_nn = D_n,
+        // keeping T_qn in fp32 MFMA accumulators: with k = 4g + i at step i a
+        // lane's accumulator element i is exactly its B operand, so no block
+        // goes back through LDS.  Every block is written once, scaled by beta of
+        // its column and rounded, into the MFMA operand array Tp.
         {
             float(*L)[SM::LP] = sm.L;
-            float(*Ti)[SM::LP] = sm.x.Ti;
+            float(*Ti)[SM::LP] = sm.x.Ti;  // only the diagonal blocks are used
             if (w == 0) {
-                // column cc of the inverse of the unit lower diagonal block mb
                 const int mb = l >> 4, cc = l & 15, o0 = 16 * mb;
+                const float bc = sm.beta[o0 + cc];
                 float xv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -476,54 +483,44 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
                     xv[r] = acc;
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) Ti[o0 + r][o0 + cc] = xv[r];
+                for (int r = 0; r < 16; ++r) {
+                    Ti[o0 + r][o0 + cc] = xv[r];
+                    sm.y.Tp[o0 + r][o0 + cc] = from_f<T>(xv[r] * bc);
+                }
             } else {
                 for (int e = t - 64; e < 6 * 256; e += 192) {  // upper off-diagonal blocks are zero
                     const int bi = e / 256, a = (e / 16) % 16, b = e % 16;
                     const int mb = (bi < 3) ? 0 : (bi < 5 ? 1 : 2);
                     const int nb = (bi < 3) ? bi + 1 : (bi < 5 ? bi - 1 : 3);
-                    Ti[16 * mb + a][16 * nb + b] = 0.f;
+                    sm.y.Tp[16 * mb + a][16 * nb + b] = from_f<T>(0.f);
                 }
             }
             lds_barrier();
-            // Ti_mn = -Ti_mm sum_{q=n}^{m-1} L_mq Ti_qn, block row by block row; wave n
-            // computes block column n with fp32 MFMA (16x16x4, k = 4e + g at step e).
+            if (w < 3) {
+                const int n = w;
+                const float bc = sm.beta[16 * n + x];
+                f32x4 Tr[4];  // Tr[d] = T_{n+d, n}: rows 4g + i, column x
 #pragma unroll
-            for (int m = 1; m < 4; ++m) {
-                if (w < m) {
-                    const int n = w;
+                for (int i = 0; i < 4; ++i) Tr[0][i] = Ti[16 * n + 4 * g + i][16 * n + x];
+#pragma unroll
+                for (int d = 1; d < 4; ++d) {
+                    if (n + d > 3) break;
+                    const int m = n + d;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int qb = 0; qb < m; ++qb)
-                        if (qb >= n)
+                    for (int qd = 0; qd < d; ++qd) {
+                        const f32x4 a = *reinterpret_cast<const f32x4 *>(&L[16 * m + x][16 * (n + qd) + 4 * g]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(L[16 * m + x][16 * qb + 4 * e + g],
-                                                                       Ti[16 * qb + 4 * e + g][16 * n + x], acc, 0, 0, 0);
+                        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], Tr[qd][i], acc, 0, 0, 0);
+                    }
+                    const f32x4 dm = *reinterpret_cast<const f32x4 *>(&Ti[16 * m + x][16 * m + 4 * g]);
+                    f32x4 tm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) L[16 * n + 4 * g + ii][16 * m + x] = acc[ii];  // scratch
+                    for (int i = 0; i < 4; ++i) tm = __builtin_amdgcn_mfma_f32_16x16x4f32(dm[i], acc[i], tm, 0, 0, 0);
+                    Tr[d] = -tm;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sm.y.Tp[16 * m + 4 * g + i][16 * n + x] = from_f<T>(Tr[d][i] * bc);
                 }
-                lds_barrier();
-                if (w < m) {
-                    const int n = w;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ti[16 * m + x][16 * m + 4 * e + g],
-                                                                   L[16 * n + 4 * e + g][16 * m + x], acc, 0, 0, 0);
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) Ti[16 * m + 4 * g + ii][16 * n + x] = -acc[ii];
-                }
-                lds_barrier();
-            }
-            {
-                const int k2 = t % CHUNK, r0 = t / CHUNK;  // column k2, rows r0, r0+4, ...
-                const float bk = sm.beta[k2];
-                float tv[CHUNK / 4];
-#pragma unroll
-                for (int j = 0; j < CHUNK / 4; ++j) tv[j] = Ti[r0 + 4 * j][k2];
-#pragma unroll
-                for (int j = 0; j < CHUNK / 4; ++j) sm.y.Tp[r0 + 4 * j][k2] = from_f<T>(tv[j] * bk);
             }
         }
         lds_barrier();
