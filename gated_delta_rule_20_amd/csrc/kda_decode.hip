@@ -13,11 +13,11 @@
 // so one pass over S yields both reductions, and the update is applied while
 // the rows are still in registers.
 //
-// Launch: two 256-thread workgroups per (sequence, head), each owning half of
-// the d_v columns (columns evolve independently; twice the workgroups balance
-// the 1 GiB stream better over the compute units).  Thread t owns the 4
-// columns c0 + 4*(t % CG) .. +3 (CG = column groups of the half) and rows
-// (t / CG) + RG*i (RG = 256 / CG row groups), so each load instruction of a
+// Launch: two 128-thread workgroups per (sequence, head), each owning half of
+// the d_v columns (columns evolve independently; small workgroups balance the
+// 1 GiB stream better over the compute units).  Thread t owns the 4 columns
+// c0 + 4*(t % CG) .. +3 (CG = column groups of the half) and rows
+// (t / CG) + RG*i (RG = 128 / CG row groups), so each load instruction of a
 // wave covers whole rows of the half (coalesced 16-byte accesses).  The two
 // column reductions go through LDS once.  The state is read and written with
 // non-temporal hints: it is streamed once per step and never re-read soon.
@@ -26,16 +26,16 @@
 namespace kda {
 
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void recurrent_step_kernel(
+__global__ __launch_bounds__(128) void recurrent_step_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ gz, const T *__restrict__ beta, const float *__restrict__ A_log,
     float g_min, float scale, int H, float *__restrict__ state, T *__restrict__ o)
 {
     constexpr int WC = DV / 2;          // columns handled by this workgroup
     constexpr int CG = WC / 4;          // column groups of 4
-    constexpr int RG = 256 / CG;        // row groups
+    constexpr int RG = 128 / CG;        // row groups
     constexpr int RPT = DK / RG;        // rows per thread
-    static_assert(RPT * RG == DK, "row split");
+    static_assert(RPT * RG == DK && DK <= 128, "row split; threads 0..DK-1 stage k, q, alpha");
 
     __shared__ float s_k[DK], s_q[DK], s_a[DK];
     __shared__ float s_red[2][RG][WC];
@@ -112,7 +112,7 @@ hipError_t launch_step_t(int N, int H, const void *q, const void *k, const void 
                          float *state, void *o, hipStream_t stream)
 {
     const unsigned grid = (unsigned)((size_t)N * H * 2);
-    hipLaunchKernelGGL((recurrent_step_kernel<T, DK, DV>), dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL((recurrent_step_kernel<T, DK, DV>), dim3(grid), dim3(128), 0, stream,
                        (const T *)q, (const T *)k, (const T *)v, (const T *)g, (const T *)beta,
                        A_log, g_min, scale, H, state, (T *)o);
     return hipGetLastError();
