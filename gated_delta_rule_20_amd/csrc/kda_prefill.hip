@@ -175,7 +175,7 @@ template <typename T, int DK, int DV> struct IntraSmem {
     } y;
     T KpT[DK][PT];         // (k * exp(lam))^T, A operand of W^T
     T VT[DV][PT];          // v^T, B operand of U
-    float tot[4][DK];      // tile totals T_m (log2 units)
+    float tot[8][DK];      // half-tile (8-token segment) totals (log2 units)
     float beta[CHUNK];
 };
 
@@ -186,16 +186,21 @@ __device__ __forceinline__ int colop_row(int m, int n)
     return (n == 0) ? (m == 2 ? 112 : 128) : 144;
 }
 
+// Eight waves; wave w owns the 8-token half-tile (segment) 2*(w % 4) + w / 4,
+// i.e. tokens seg_base(w) .. +7 of sub-tile w % 4.
+constexpr int IWAVES = 8, HT = SUB / 2;
+__device__ __forceinline__ int seg_base(int w) { return SUB * (w & 3) + HT * (w >> 2); }
+
 // Raw inputs of one (chunk, head) in registers, unconverted (converting at
 // load time would make the wave wait for the loads): lane l of wave w holds
-// channels CPT*l.. of tokens 16w..16w+15 of g, k, q, value columns CPV*l.. of
-// the same tokens, and (lanes 0..15) beta of token 16w + l.
+// channels CPT*l.. of the wave's 8 tokens of g, k, q, value columns CPV*l..
+// of the same tokens, and (lanes 0..7) beta of token seg_base(w) + l.
 template <typename T, int DK, int DV> struct RawIn {
     static constexpr int CPT = DK / 64, CPV = DV / 64;
     typedef typename Vec<T, CPT>::type ku;
     typedef typename Vec<T, CPV>::type vu;
-    ku g[SUB], k[SUB], q[SUB];
-    vu v[SUB];
+    ku g[HT], k[HT], q[HT];
+    vu v[HT];
     T beta;
     float alog;
 };
@@ -214,9 +219,10 @@ __device__ __forceinline__ void load_raw(RawIn<T, DK, DV> &in, const PrefillPara
     for (int c = 0; c < R::CPT; ++c) zk[c] = from_f<T>(0.f);
 #pragma unroll
     for (int c = 0; c < R::CPV; ++c) zv[c] = from_f<T>(0.f);
+    const int tb = seg_base(w);
 #pragma unroll
-    for (int r = 0; r < SUB; ++r) {
-        const int tok = SUB * w + r;
+    for (int r = 0; r < HT; ++r) {
+        const int tok = tb + r;
         const bool ok = tok < len;
         const size_t row = (size_t)(tok0 + tok) * p.H + h;
         in.g[r] = ok ? *reinterpret_cast<const ku *>(gg + row * DK + R::CPT * l) : zk;
@@ -224,8 +230,8 @@ __device__ __forceinline__ void load_raw(RawIn<T, DK, DV> &in, const PrefillPara
         in.q[r] = ok ? *reinterpret_cast<const ku *>(qg + row * DK + R::CPT * l) : zk;
         in.v[r] = ok ? *reinterpret_cast<const vu *>(vg + row * DV + R::CPV * l) : zv;
     }
-    const int bt = SUB * w + l;
-    in.beta = (l < SUB && bt < len) ? ((const T *)p.beta)[(size_t)(tok0 + bt) * p.H + h] : from_f<T>(0.f);
+    const int bt = tb + l;
+    in.beta = (l < HT && bt < len) ? ((const T *)p.beta)[(size_t)(tok0 + bt) * p.H + h] : from_f<T>(0.f);
     in.alog = p.A_log ? p.A_log[h] : 0.f;
 }
 
@@ -264,34 +270,22 @@ __device__ __forceinline__ bool next_item(const PrefillParams &p, int &i, int &c
     return false;
 }
 
-// (m, n) sub-tile pairs (n <= m) handled by wave w in step s, as the index
-// m(m+1)/2 + n; -1 = none.  Balances the 10 pairs over 4 waves as 3/3/2/2.
-__device__ __forceinline__ int pair_of(int w, int s)
-{
-    switch (w * 3 + s) {
-    case 0: return 0; case 1: return 2; case 2: return 5;
-    case 3: return 9; case 4: return 1; case 5: return 4;
-    case 6: return 8; case 7: return 3;
-    case 9: return 7; case 10: return 6;
-    default: return -1;
-    }
-}
-
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
+__global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 {
     using BL = Block<T, DK, DV>;
     using SM = IntraSmem<T, DK, DV>;
     using R = RawIn<T, DK, DV>;
     constexpr int KS = DK / 32, RT = DK / 64, CPT = R::CPT, CPV = R::CPV;
     typedef typename R::ku ku;
-    typedef typename Vec<T, SUB>::type tok16;
+    typedef typename Vec<T, HT>::type tok8;
     typedef typename Vec<T, 4>::type tok4;
     extern __shared__ __align__(16) char smem_raw[];
     SM &sm = *reinterpret_cast<SM *>(smem_raw);
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, x = l & 15;
     const int ch0 = CPT * l;  // first channel of this lane in the elementwise phase
+    const int m0 = w & 3, hf = w >> 2, tb = seg_base(w);  // elementwise: tile, half, first token
 
     int i = blockIdx.x, c, h, tok0, len;
     bool have = next_item(p, i, c, h, tok0, len);
@@ -308,7 +302,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
         // loop); wait for them once here rather than at a conservative point
         // behind this item's first store.
         __builtin_amdgcn_s_waitcnt(0);
-        float lam2[SUB][CPT];  // (lam_r - B_w) log2(e) for this wave's tokens
+        float lam2[HT][CPT];  // (lam_r - B_m) log2(e) for this wave's tokens (tile m = w % 4)
         {
             const float cz = -__expf(raw.alog) * LOG2E;  // exp(-e^A z) = exp2(cz z)
             const float gm2 = p.g_min * LOG2E;
@@ -316,48 +310,53 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) run[cc] = 0.f;
 #pragma unroll
-            for (int r = 0; r < SUB; ++r) {
+            for (int r = 0; r < HT; ++r) {
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) {
                     const float z = to_f<T>(raw.g[r][cc]);
                     float g2 = p.A_log ? gm2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(cz * z))
                                        : clamp_logdecay(z, p.g_min) * LOG2E;
-                    g2 = (SUB * w + r < len) ? g2 : 0.f;  // tokens past the end keep S unchanged
+                    g2 = (tb + r < len) ? g2 : 0.f;  // tokens past the end keep S unchanged
                     run[cc] += g2;
                     lam2[r][cc] = run[cc];
                 }
             }
 #pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) sm.tot[w][ch0 + cc] = run[cc];
-            if (l < SUB) sm.beta[SUB * w + l] = to_f<T>(raw.beta);
+            for (int cc = 0; cc < CPT; ++cc) sm.tot[2 * m0 + hf][ch0 + cc] = run[cc];
+            if (l < HT) sm.beta[tb + l] = to_f<T>(raw.beta);
         }
         lds_barrier();
         {
             float eBm[CPT], eCB[CPT], eT[CPT], eX1[CPT], eX2[CPT], gC[CPT];
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) {
-                const float t0 = sm.tot[0][ch0 + cc], t1 = sm.tot[1][ch0 + cc];
-                const float t2 = sm.tot[2][ch0 + cc], t3 = sm.tot[3][ch0 + cc];
-                const float Bm = (w > 0 ? t0 : 0.f) + (w > 1 ? t1 : 0.f) + (w > 2 ? t2 : 0.f);
+                float sg[8];
+#pragma unroll
+                for (int q2 = 0; q2 < 8; ++q2) sg[q2] = sm.tot[q2][ch0 + cc];
+                const float t0 = sg[0] + sg[1], t1 = sg[2] + sg[3], t2 = sg[4] + sg[5], t3 = sg[6] + sg[7];
+                const float Bm = (m0 > 0 ? t0 : 0.f) + (m0 > 1 ? t1 : 0.f) + (m0 > 2 ? t2 : 0.f);
                 const float C2 = t0 + t1 + t2 + t3;
-                eBm[cc] = __builtin_amdgcn_exp2f(Bm);              // exp(B_w)            <= 1
-                eCB[cc] = __builtin_amdgcn_exp2f(C2 - Bm);         // exp(lam_C - B_w)    <= 1
-                const float Tw = (w == 0) ? t0 : (w == 1 ? t1 : (w == 2 ? t2 : t3));
-                eT[cc] = __builtin_amdgcn_exp2f(Tw);               // exp(T_w): reference moved to the tile end
-                eX1[cc] = __builtin_amdgcn_exp2f(w == 0 ? t1 : t2);  // tile 0 -> B_2, tile 1 -> B_3
-                eX2[cc] = __builtin_amdgcn_exp2f(t1 + t2);           // tile 0 -> B_3
+                const float hoff = hf ? sg[2 * m0] : 0.f;          // first half of the tile, for the second half
+#pragma unroll
+                for (int r = 0; r < HT; ++r) lam2[r][cc] += hoff;
+                eBm[cc] = __builtin_amdgcn_exp2f(Bm);              // exp(B_m)            <= 1
+                eCB[cc] = __builtin_amdgcn_exp2f(C2 - Bm);         // exp(lam_C - B_m)    <= 1
+                const float Tw = (m0 == 0) ? t0 : (m0 == 1 ? t1 : (m0 == 2 ? t2 : t3));
+                eT[cc] = __builtin_amdgcn_exp2f(Tw);               // exp(T_m): reference moved to the tile end
+                eX1[cc] = __builtin_amdgcn_exp2f(m0 == 0 ? t1 : t2);  // tile 0 -> B_2, tile 1 -> B_3
+                eX2[cc] = __builtin_amdgcn_exp2f(t1 + t2);            // tile 0 -> B_3
                 gC[cc] = __builtin_amdgcn_exp2f(C2);
             }
-            tok16 kpv[CPT], ktv[CPT];
+            tok8 kpv[CPT], ktv[CPT];
 #pragma unroll
-            for (int r = 0; r < SUB; ++r) {
-                const int tok = SUB * w + r;
+            for (int r0 = 0; r0 < HT; ++r0) {
+                const int r = HT * hf + r0, tok = tb + r0;  // r: token within the tile
                 ku kr_, qr_, kc_, ke_, kx1_, kx2_, qp_;
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) {
-                    const float kv = to_f<T>(raw.k[r][cc]);
-                    const float qv = p.scale * to_f<T>(raw.q[r][cc]);
-                    const float eR = __builtin_amdgcn_exp2f(lam2[r][cc]);        // exp(lam_r - B_w) <= 1
+                    const float kv = to_f<T>(raw.k[r0][cc]);
+                    const float qv = p.scale * to_f<T>(raw.q[r0][cc]);
+                    const float eR = __builtin_amdgcn_exp2f(lam2[r0][cc]);        // exp(lam_r - B_w) <= 1
                     const float eC = __builtin_amdgcn_rcpf(eR);  // exp(B_w - lam_r) <= e^80
                     const float kr = kv * eR, qr = qv * eR, kcs = kv * eC, kce = kcs * eT[cc];
                     kr_[cc] = from_f<T>(kr);
@@ -367,37 +366,38 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
                     kx1_[cc] = from_f<T>(kce * eX1[cc]);
                     kx2_[cc] = from_f<T>(kce * eX2[cc]);
                     qp_[cc] = from_f<T>(qr * eBm[cc]);
-                    kpv[cc][r] = from_f<T>(kr * eBm[cc]);
-                    ktv[cc][r] = from_f<T>(kcs * eCB[cc]);
+                    kpv[cc][r0] = from_f<T>(kr * eBm[cc]);
+                    ktv[cc][r0] = from_f<T>(kcs * eCB[cc]);
                 }
                 *reinterpret_cast<ku *>(&sm.x.ops.KR[tok][ch0]) = kr_;
                 *reinterpret_cast<ku *>(&sm.x.ops.QR[tok][ch0]) = qr_;
                 *reinterpret_cast<ku *>(&sm.y.KC[tok][ch0]) = kc_;
-                if (w < 3) *reinterpret_cast<ku *>(&sm.y.KC[64 + tok][ch0]) = ke_;
-                if (w == 0) {
+                if (m0 < 3) *reinterpret_cast<ku *>(&sm.y.KC[64 + tok][ch0]) = ke_;
+                if (m0 == 0) {
                     *reinterpret_cast<ku *>(&sm.y.KC[112 + r][ch0]) = kx1_;
                     *reinterpret_cast<ku *>(&sm.y.KC[128 + r][ch0]) = kx2_;
                 }
-                if (w == 1) *reinterpret_cast<ku *>(&sm.y.KC[144 + r][ch0]) = kx1_;
+                if (m0 == 1) *reinterpret_cast<ku *>(&sm.y.KC[144 + r][ch0]) = kx1_;
                 // Q+ as the chain's operand fragment (kmap along channels): token tok ->
                 // wave w, lane r + 16 gq, element 4 half + ch0 % 4 of k-step ch0 / 32
                 {
                     const int cq = ch0 % 32, hq = cq / 16, gq = (cq % 16) / 4;
-                    *reinterpret_cast<ku *>(blk + BL::Q_OFF + ((w * KS + ch0 / 32) * 64 + r + 16 * gq) * 8 + 4 * hq +
+                    *reinterpret_cast<ku *>(blk + BL::Q_OFF + ((m0 * KS + ch0 / 32) * 64 + r + 16 * gq) * 8 + 4 * hq +
                                             cq % 4) = qp_;
                 }
             }
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) {
                 const int ch = ch0 + cc;
-                *reinterpret_cast<tok16 *>(&sm.KpT[ch][SUB * w]) = kpv[cc];
+                *reinterpret_cast<tok8 *>(&sm.KpT[ch][tb]) = kpv[cc];
                 // (K gamma^C / Gamma)^T fragments of the chain: rows = channels, k = tokens (kmap)
-                const int wq = ch / (16 * RT), rt = (ch / 16) % RT, xq = ch % 16, ks = w / 2, half = w % 2;
+                const int wq = ch / (16 * RT), rt = (ch / 16) % RT, xq = ch % 16, ks = m0 / 2, half = m0 % 2;
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
+                for (int gg = 0; gg < 2; ++gg) {
+                    const int gq = 2 * hf + gg;
                     tok4 q4;
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) q4[ii] = ktv[cc][4 * gq + ii];
+                    for (int ii = 0; ii < 4; ++ii) q4[ii] = ktv[cc][4 * gg + ii];
                     *reinterpret_cast<tok4 *>(blk + BL::KT_OFF + (((wq * RT + rt) * 2 + ks) * 64 + xq + 16 * gq) * 8 +
                                               4 * half) = q4;
                 }
@@ -408,10 +408,10 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
             }
 #pragma unroll
             for (int cv = 0; cv < CPV; ++cv) {
-                tok16 col;
+                tok8 col;
 #pragma unroll
-                for (int r = 0; r < SUB; ++r) col[r] = raw.v[r][cv];
-                *reinterpret_cast<tok16 *>(&sm.VT[CPV * l + cv][SUB * w]) = col;
+                for (int r = 0; r < HT; ++r) col[r] = raw.v[r][cv];
+                *reinterpret_cast<tok8 *>(&sm.VT[CPV * l + cv][tb]) = col;
             }
         }
         // prefetch the next item's raw inputs (the registers are free now)
@@ -423,9 +423,9 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
         // ---- P2: L and A sub-tiles on MFMA ----------------------------------
         {
 #pragma unroll
-            for (int s = 0; s < 3; ++s) {
-                const int pi = pair_of(w, s);
-                if (pi < 0) break;
+            for (int s = 0; s < 2; ++s) {
+                const int pi = w + IWAVES * s;  // (m, n) pair m(m+1)/2 + n; waves 0, 1 take two
+                if (pi >= 10) break;
                 const int m = (pi == 0) ? 0 : (pi < 3 ? 1 : (pi < 6 ? 2 : 3));
                 const int n = pi - m * (m + 1) / 2;
                 const int cr = colop_row(m, n);
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
                 *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
                     make_quad<T>(a4);
             }
-            if (w >= 2) {  // the all-zero upper tiles inside used k-steps: (0,1) and (2,3)
+            if (w == 2 || w == 3) {  // the all-zero upper tiles inside used k-steps: (0,1) and (2,3)
                 const int m = (w == 2) ? 0 : 2, n = m + 1;
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
                     sm.y.Tp[o0 + r][o0 + cc] = from_f<T>(xv[r] * bc);
                 }
             } else {
-                for (int e = t - 64; e < 6 * 256; e += 192) {  // upper off-diagonal blocks are zero
+                for (int e = t - 64; e < 6 * 256; e += 64 * (IWAVES - 1)) {  // upper off-diagonal blocks are zero
                     const int bi = e / 256, a = (e / 16) % 16, b = e % 16;
                     const int mb = (bi < 3) ? 0 : (bi < 5 ? 1 : 2);
                     const int nb = (bi < 3) ? bi + 1 : (bi < 5 ? bi - 1 : 3);
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
         lds_barrier();
 
         // ---- P4: U = T' V and W^T = K+^T T'^T on MFMA -------------------------
-        for (int ct = w; ct < DV / 16; ct += 4) {
+        for (int ct = w; ct < DV / 16; ct += IWAVES) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(PrefillParams p)
                 *reinterpret_cast<quad_t<T> *>(blk + BL::U_OFF + ((ct * 4 + m) * 64 + l) * 4) = make_quad<T>(acc);
             }
         }
-        for (int ct = w; ct < DK / 16; ct += 4) {
+        for (int ct = w; ct < DK / 16; ct += IWAVES) {
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -778,7 +778,7 @@ static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
         if (attr != hipSuccess) return attr;
         const long items = (long)p.n_chunks_cap * p.H;
         const unsigned grid = (unsigned)(items < intra_grid() ? items : intra_grid());
-        hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV>), dim3(grid), dim3(256), smem, st, p);
+        hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV>), dim3(grid), dim3(64 * IWAVES), smem, st, p);
     }
     const long npairs = (long)p.N * p.H;
     const unsigned grid = (unsigned)(((npairs + 7) / 8) * 8 * (DV / 16));
