@@ -161,23 +161,32 @@ template <typename T, int DK, int DV> struct IntraSmem {
     // [64,112) exp(B_{n+1} - lam) for tiles 0..2 (pairs (n+1, n)); [112,128)
     // tile 0 at B_2; [128,144) tile 0 at B_3; [144,160) tile 1 at B_3.
     static constexpr int NCOL = 160;
-    union {
-        struct {
-            T KR[CHUNK][PR];   // k * exp(lam - B_m): row operand of L
-            T QR[CHUNK][PR];   // scale * q * exp(lam - B_m): row operand of A
-        } ops;                 // P1 -> P2
-        float Ti[CHUNK][LP];   // (I + L)^-1 (P3)
-    } x;
-    float L[CHUNK][LP];        // Diag(beta) StrictTril(...); upper blocks serve as scratch (P2 -> P3)
+    struct {
+        T KR[CHUNK][PR];   // k * exp(lam - B_m): row operand of L (P1 -> P2)
+        T QR[CHUNK][PR];   // scale * q * exp(lam - B_m): row operand of A (P1 -> P3)
+    } ops;
+    // Lower 16x16 blocks: Diag(beta) StrictTril(K+ K-^T) (P2 -> P3); four of the
+    // unused upper blocks hold the diagonal inverses D_m (P3), see dblk().
+    float L[CHUNK][LP];
     union {
         T KC[NCOL][PR];    // column operands (P1 -> P2)
-        T Tp[CHUNK][PT];   // (I + L)^-1 Diag(beta) (P3 -> P4)
+        struct {
+            T keep[CHUNK][PR];  // diagonal column operands (not reused)
+            T Tp[CHUNK][PT];    // (I + L)^-1 Diag(beta) (P3 -> P4)
+        } t;
     } y;
     T KpT[DK][PT];         // (k * exp(lam))^T, A operand of W^T
     T VT[DV][PT];          // v^T, B operand of U
     float tot[8][DK];      // half-tile (8-token segment) totals (log2 units)
+    float eB[4][DK];       // exp(B_m) per tile and channel (P1 -> P3)
     float beta[CHUNK];
 };
+
+// Upper block of L that holds D_m = (I + L_mm)^-1: (0,1), (0,2), (0,3), (1,2).
+template <typename SM> __device__ __forceinline__ float *dblk(SM &sm, int m)
+{
+    return &sm.L[m == 3 ? 16 : 0][m == 3 ? 32 : 16 * (m + 1)];
+}
 
 __device__ __forceinline__ int colop_row(int m, int n)
 {
@@ -347,11 +356,15 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 eX2[cc] = __builtin_amdgcn_exp2f(t1 + t2);            // tile 0 -> B_3
                 gC[cc] = __builtin_amdgcn_exp2f(C2);
             }
+            if (hf == 0) {
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) sm.eB[m0][ch0 + cc] = eBm[cc];
+            }
             tok8 kpv[CPT], ktv[CPT];
 #pragma unroll
             for (int r0 = 0; r0 < HT; ++r0) {
                 const int r = HT * hf + r0, tok = tb + r0;  // r: token within the tile
-                ku kr_, qr_, kc_, ke_, kx1_, kx2_, qp_;
+                ku kr_, qr_, kc_, ke_, kx1_, kx2_;
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) {
                     const float kv = to_f<T>(raw.k[r0][cc]);
@@ -365,12 +378,11 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     ke_[cc] = from_f<T>(kce);
                     kx1_[cc] = from_f<T>(kce * eX1[cc]);
                     kx2_[cc] = from_f<T>(kce * eX2[cc]);
-                    qp_[cc] = from_f<T>(qr * eBm[cc]);
                     kpv[cc][r0] = from_f<T>(kr * eBm[cc]);
                     ktv[cc][r0] = from_f<T>(kcs * eCB[cc]);
                 }
-                *reinterpret_cast<ku *>(&sm.x.ops.KR[tok][ch0]) = kr_;
-                *reinterpret_cast<ku *>(&sm.x.ops.QR[tok][ch0]) = qr_;
+                *reinterpret_cast<ku *>(&sm.ops.KR[tok][ch0]) = kr_;
+                *reinterpret_cast<ku *>(&sm.ops.QR[tok][ch0]) = qr_;
                 *reinterpret_cast<ku *>(&sm.y.KC[tok][ch0]) = kc_;
                 if (m0 < 3) *reinterpret_cast<ku *>(&sm.y.KC[64 + tok][ch0]) = ke_;
                 if (m0 == 0) {
@@ -378,13 +390,6 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     *reinterpret_cast<ku *>(&sm.y.KC[128 + r][ch0]) = kx2_;
                 }
                 if (m0 == 1) *reinterpret_cast<ku *>(&sm.y.KC[144 + r][ch0]) = kx1_;
-                // Q+ as the chain's operand fragment (kmap along channels): token tok ->
-                // wave w, lane r + 16 gq, element 4 half + ch0 % 4 of k-step ch0 / 32
-                {
-                    const int cq = ch0 % 32, hq = cq / 16, gq = (cq % 16) / 4;
-                    *reinterpret_cast<ku *>(blk + BL::Q_OFF + ((m0 * KS + ch0 / 32) * 64 + r + 16 * gq) * 8 + 4 * hq +
-                                            cq % 4) = qp_;
-                }
             }
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) {
@@ -432,8 +437,8 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 f32x4 aL = {0.f, 0.f, 0.f, 0.f}, aA = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const frag_t<T> kr = load_frag_lin<T>(&sm.x.ops.KR[16 * m + x][32 * ks], g);
-                    const frag_t<T> qr = load_frag_lin<T>(&sm.x.ops.QR[16 * m + x][32 * ks], g);
+                    const frag_t<T> kr = load_frag_lin<T>(&sm.ops.KR[16 * m + x][32 * ks], g);
+                    const frag_t<T> qr = load_frag_lin<T>(&sm.ops.QR[16 * m + x][32 * ks], g);
                     const frag_t<T> kc = load_frag_lin<T>(&sm.y.KC[cr + x][32 * ks], g);
                     aL = mma(kr, kc, aL);   // rows r (tile m), cols i (tile n)
                     aA = mma(kc, qr, aA);   // rows i (tile n), cols r (tile m): A^T
@@ -459,7 +464,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     make_quad<T>(z);
             }
         }
-        lds_barrier();  // L complete; KR / QR / KC fully read (Ti may overwrite them)
+        lds_barrier();  // L complete; KR / KC fully read (Tp may overwrite the off-diagonal column operands)
         // ---- P3: T' = (I + L)^-1 Diag(beta), 16x16 blocks ---------------------
         // Diagonal blocks D_m = (I + L_mm)^-1 by substitution (wave 0, one lane
         // per (block, column)); then wave n < 3 walks block column n downwards,
@@ -470,7 +475,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         // its column and rounded, into the MFMA operand array Tp.
         {
             float(*L)[SM::LP] = sm.L;
-            float(*Ti)[SM::LP] = sm.x.Ti;  // only the diagonal blocks are used
+            constexpr int LP = SM::LP;
             if (w == 0) {
                 const int mb = l >> 4, cc = l & 15, o0 = 16 * mb;
                 const float bc = sm.beta[o0 + cc];
@@ -482,17 +487,18 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     for (int k2 = 0; k2 < r; ++k2) acc -= L[o0 + r][o0 + k2] * xv[k2];
                     xv[r] = acc;
                 }
+                float *Dm = dblk(sm, mb);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    Ti[o0 + r][o0 + cc] = xv[r];
-                    sm.y.Tp[o0 + r][o0 + cc] = from_f<T>(xv[r] * bc);
+                    Dm[r * LP + cc] = xv[r];
+                    sm.y.t.Tp[o0 + r][o0 + cc] = from_f<T>(xv[r] * bc);
                 }
             } else {
                 for (int e = t - 64; e < 6 * 256; e += 64 * (IWAVES - 1)) {  // upper off-diagonal blocks are zero
                     const int bi = e / 256, a = (e / 16) % 16, b = e % 16;
                     const int mb = (bi < 3) ? 0 : (bi < 5 ? 1 : 2);
                     const int nb = (bi < 3) ? bi + 1 : (bi < 5 ? bi - 1 : 3);
-                    sm.y.Tp[16 * mb + a][16 * nb + b] = from_f<T>(0.f);
+                    sm.y.t.Tp[16 * mb + a][16 * nb + b] = from_f<T>(0.f);
                 }
             }
             lds_barrier();
@@ -501,7 +507,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 const float bc = sm.beta[16 * n + x];
                 f32x4 Tr[4];  // Tr[d] = T_{n+d, n}: rows 4g + i, column x
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Tr[0][i] = Ti[16 * n + 4 * g + i][16 * n + x];
+                for (int i = 0; i < 4; ++i) Tr[0][i] = dblk(sm, n)[(4 * g + i) * LP + x];
 #pragma unroll
                 for (int d = 1; d < 4; ++d) {
                     if (n + d > 3) break;
@@ -513,13 +519,29 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], Tr[qd][i], acc, 0, 0, 0);
                     }
-                    const f32x4 dm = *reinterpret_cast<const f32x4 *>(&Ti[16 * m + x][16 * m + 4 * g]);
+                    const f32x4 dm = *reinterpret_cast<const f32x4 *>(dblk(sm, m) + x * LP + 4 * g);
                     f32x4 tm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) tm = __builtin_amdgcn_mfma_f32_16x16x4f32(dm[i], acc[i], tm, 0, 0, 0);
                     Tr[d] = -tm;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sm.y.Tp[16 * m + 4 * g + i][16 * n + x] = from_f<T>(Tr[d][i] * bc);
+                    for (int i = 0; i < 4; ++i) sm.y.t.Tp[16 * m + 4 * g + i][16 * n + x] = from_f<T>(Tr[d][i] * bc);
+                }
+            } else {
+                // Q+ = scale Q Gamma as the chain's operand fragments (rows tokens, k
+                // channels in kmap order), from the row operand and exp(B_m).
+                for (int f = w - 3; f < 4 * KS; f += IWAVES - 3) {
+                    const int m = f / KS, ks = f % KS;
+                    const frag_t<T> qr = load_frag_kmap<T>(&sm.ops.QR[16 * m + x][32 * ks], g);
+                    const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 4 * g]);
+                    const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 16 + 4 * g]);
+                    frag_t<T> qp;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        qp[e] = from_f<T>(to_f<T>(qr[e]) * e0[e]);
+                        qp[4 + e] = from_f<T>(to_f<T>(qr[4 + e]) * e1[e]);
+                    }
+                    store8(blk + BL::Q_OFF + ((m * KS + ks) * 64 + l) * 8, qp);
                 }
             }
         }
@@ -531,7 +553,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             for (int m = 0; m < 4; ++m) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 for (int ks = 0; ks <= m / 2; ++ks)
-                    acc = mma(load_frag_lin<T>(&sm.y.Tp[16 * m + x][32 * ks], g),
+                    acc = mma(load_frag_lin<T>(&sm.y.t.Tp[16 * m + x][32 * ks], g),
                               load_frag_lin<T>(&sm.VT[16 * ct + x][32 * ks], g), acc);
                 *reinterpret_cast<quad_t<T> *>(blk + BL::U_OFF + ((ct * 4 + m) * 64 + l) * 4) = make_quad<T>(acc);
             }
@@ -542,7 +564,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 for (int ks = 0; ks <= tt / 2; ++ks)
                     acc = mma(load_frag_lin<T>(&sm.KpT[16 * ct + x][32 * ks], g),
-                              load_frag_lin<T>(&sm.y.Tp[16 * tt + x][32 * ks], g), acc);
+                              load_frag_lin<T>(&sm.y.t.Tp[16 * tt + x][32 * ks], g), acc);
                 *reinterpret_cast<quad_t<T> *>(blk + BL::W_OFF + ((tt * KS + ct / 2) * 64 + l) * 8 + 4 * (ct % 2)) =
                     make_quad<T>(-acc);
             }
