@@ -176,6 +176,7 @@ template <typename T, int DK, int DV> struct IntraSmem {
         } t;
     } y;
     T KpT[DK][PT];         // (k * exp(lam))^T, A operand of W^T
+    T KtT[DK][PT];         // (k * exp(lam_C - lam))^T, copied out as the chain's K~^T fragments (P1 -> P3)
     T VT[DV][PT];          // v^T, B operand of U
     float tot[8][DK];      // half-tile (8-token segment) totals (log2 units)
     float eB[4][DK];       // exp(B_m) per tile and channel (P1 -> P3)
@@ -395,17 +396,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             for (int cc = 0; cc < CPT; ++cc) {
                 const int ch = ch0 + cc;
                 *reinterpret_cast<tok8 *>(&sm.KpT[ch][tb]) = kpv[cc];
-                // (K gamma^C / Gamma)^T fragments of the chain: rows = channels, k = tokens (kmap)
-                const int wq = ch / (16 * RT), rt = (ch / 16) % RT, xq = ch % 16, ks = m0 / 2, half = m0 % 2;
-#pragma unroll
-                for (int gg = 0; gg < 2; ++gg) {
-                    const int gq = 2 * hf + gg;
-                    tok4 q4;
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) q4[ii] = ktv[cc][4 * gg + ii];
-                    *reinterpret_cast<tok4 *>(blk + BL::KT_OFF + (((wq * RT + rt) * 2 + ks) * 64 + xq + 16 * gq) * 8 +
-                                              4 * half) = q4;
-                }
+                *reinterpret_cast<tok8 *>(&sm.KtT[ch][tb]) = ktv[cc];
             }
             if (w == 0) {  // gamma^C, stored after the last use of the raw registers
 #pragma unroll
@@ -528,6 +519,12 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     for (int i = 0; i < 4; ++i) sm.y.t.Tp[16 * m + 4 * g + i][16 * n + x] = from_f<T>(Tr[d][i] * bc);
                 }
             } else {
+                // (K gamma^C / Gamma)^T as the chain's A-operand fragments (rows
+                // channels, k tokens in kmap order), copied from LDS.
+                for (int f = w - 3; f < 2 * (DK / 16); f += IWAVES - 3) {
+                    const int R = f / 2, ks = f % 2;
+                    store8(blk + BL::KT_OFF + (f * 64 + l) * 8, load_frag_kmap<T>(&sm.KtT[16 * R + x][32 * ks], g));
+                }
                 // Q+ = scale Q Gamma as the chain's operand fragments (rows tokens, k
                 // channels in kmap order), from the row operand and exp(B_m).
                 for (int f = w - 3; f < 4 * KS; f += IWAVES - 3) {
@@ -795,6 +792,7 @@ static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
         hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, p.cu, p.N, p.chunk_off, p.order);
     if (p.n_chunks_cap > 0) {
         const size_t smem = sizeof(IntraSmem<T, DK, DV>);
+        static_assert(sizeof(IntraSmem<T, DK, DV>) <= 160 * 1024, "intra-chunk LDS exceeds 160 KiB");
         static const hipError_t attr = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV>,
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (attr != hipSuccess) return attr;
