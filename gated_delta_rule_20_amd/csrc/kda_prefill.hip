@@ -312,6 +312,18 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         // loop); wait for them once here rather than at a conservative point
         // behind this item's first store.
         __builtin_amdgcn_s_waitcnt(0);
+        // The next item's raw inputs are loaded into each raw register right after
+        // its last use below, so the loads issue between this item's VALU work.
+        int i2 = i + gridDim.x, c2 = 0, h2 = 0, tok2 = 0, len2 = 0;
+        const bool have2 = next_item(p, i2, c2, h2, tok2, len2);
+        const T *ng = (const T *)p.g, *nk = (const T *)p.k, *nq = (const T *)p.q, *nv = (const T *)p.v;
+        auto nrow = [&](int r, bool &ok) {
+            ok = have2 && tb + r < len2;
+            return (size_t)(tok2 + tb + r) * p.H + h2;
+        };
+        ku zk;
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) zk[cc] = from_f<T>(0.f);
         float lam2[HT][CPT];  // (lam_r - B_m) log2(e) for this wave's tokens (tile m = w % 4)
         {
             const float cz = -__expf(raw.alog) * LOG2E;  // exp(-e^A z) = exp2(cz z)
@@ -334,6 +346,17 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) sm.tot[2 * m0 + hf][ch0 + cc] = run[cc];
             if (l < HT) sm.beta[tb + l] = to_f<T>(raw.beta);
+        }
+#pragma unroll
+        for (int r = 0; r < HT; ++r) {
+            bool ok;
+            const size_t row = nrow(r, ok);
+            raw.g[r] = ok ? *reinterpret_cast<const ku *>(ng + row * DK + ch0) : zk;
+        }
+        {
+            const int bt = tb + l;
+            raw.beta = (have2 && l < HT && bt < len2) ? ((const T *)p.beta)[(size_t)(tok2 + bt) * p.H + h2] : from_f<T>(0.f);
+            raw.alog = (have2 && p.A_log) ? p.A_log[h2] : 0.f;
         }
         lds_barrier();
         {
@@ -391,6 +414,12 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     *reinterpret_cast<ku *>(&sm.y.KC[128 + r][ch0]) = kx2_;
                 }
                 if (m0 == 1) *reinterpret_cast<ku *>(&sm.y.KC[144 + r][ch0]) = kx1_;
+                {
+                    bool ok;
+                    const size_t row = nrow(r0, ok);
+                    raw.k[r0] = ok ? *reinterpret_cast<const ku *>(nk + row * DK + ch0) : zk;
+                    raw.q[r0] = ok ? *reinterpret_cast<const ku *>(nq + row * DK + ch0) : zk;
+                }
             }
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) {
@@ -409,11 +438,16 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 for (int r = 0; r < HT; ++r) col[r] = raw.v[r][cv];
                 *reinterpret_cast<tok8 *>(&sm.VT[CPV * l + cv][tb]) = col;
             }
+            typename R::vu zv;
+#pragma unroll
+            for (int cv = 0; cv < CPV; ++cv) zv[cv] = from_f<T>(0.f);
+#pragma unroll
+            for (int r = 0; r < HT; ++r) {
+                bool ok;
+                const size_t row = nrow(r, ok);
+                raw.v[r] = ok ? *reinterpret_cast<const typename R::vu *>(nv + row * DV + CPV * l) : zv;
+            }
         }
-        // prefetch the next item's raw inputs (the registers are free now)
-        int i2 = i + gridDim.x, c2 = 0, h2 = 0, tok2 = 0, len2 = 0;
-        const bool have2 = next_item(p, i2, c2, h2, tok2, len2);
-        if (have2) load_raw(raw, p, tok2, len2, h2, w, l);
         lds_barrier();
 
         // ---- P2: L and A sub-tiles on MFMA ----------------------------------
@@ -491,6 +525,21 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     const int nb = (bi < 3) ? bi + 1 : (bi < 5 ? bi - 1 : 3);
                     sm.y.t.Tp[16 * mb + a][16 * nb + b] = from_f<T>(0.f);
                 }
+                // Q+ = scale Q Gamma as the chain's operand fragments (rows tokens, k
+                // channels in kmap order), from the row operand and exp(B_m).
+                for (int f = w - 1; f < 4 * KS; f += IWAVES - 1) {
+                    const int m = f / KS, ks = f % KS;
+                    const frag_t<T> qr = load_frag_kmap<T>(&sm.ops.QR[16 * m + x][32 * ks], g);
+                    const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 4 * g]);
+                    const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 16 + 4 * g]);
+                    frag_t<T> qp;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        qp[e] = from_f<T>(to_f<T>(qr[e]) * e0[e]);
+                        qp[4 + e] = from_f<T>(to_f<T>(qr[4 + e]) * e1[e]);
+                    }
+                    store8(blk + BL::Q_OFF + ((m * KS + ks) * 64 + l) * 8, qp);
+                }
             }
             lds_barrier();
             if (w < 3) {
@@ -524,21 +573,6 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 for (int f = w - 3; f < 2 * (DK / 16); f += IWAVES - 3) {
                     const int R = f / 2, ks = f % 2;
                     store8(blk + BL::KT_OFF + (f * 64 + l) * 8, load_frag_kmap<T>(&sm.KtT[16 * R + x][32 * ks], g));
-                }
-                // Q+ = scale Q Gamma as the chain's operand fragments (rows tokens, k
-                // channels in kmap order), from the row operand and exp(B_m).
-                for (int f = w - 3; f < 4 * KS; f += IWAVES - 3) {
-                    const int m = f / KS, ks = f % KS;
-                    const frag_t<T> qr = load_frag_kmap<T>(&sm.ops.QR[16 * m + x][32 * ks], g);
-                    const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 4 * g]);
-                    const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 16 + 4 * g]);
-                    frag_t<T> qp;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        qp[e] = from_f<T>(to_f<T>(qr[e]) * e0[e]);
-                        qp[4 + e] = from_f<T>(to_f<T>(qr[4 + e]) * e1[e]);
-                    }
-                    store8(blk + BL::Q_OFF + ((m * KS + ks) * 64 + l) * 8, qp);
                 }
             }
         }
