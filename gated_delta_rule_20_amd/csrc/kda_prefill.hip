@@ -491,55 +491,76 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         }
         lds_barrier();  // L complete; KR / KC fully read (Tp may overwrite the off-diagonal column operands)
         // ---- P3: T' = (I + L)^-1 Diag(beta), 16x16 blocks ---------------------
-        // Diagonal blocks D_m = (I + L_mm)^-1 by substitution (wave 0, one lane
-        // per (block, column)); then wave n < 3 walks block column n downwards,
+        // Diagonal blocks D_m = (I + L_mm)^-1 (waves 0-3, below); then wave
+        // n < 3 walks block column n downwards,
         //   T_mn = -D_m sum_{q=n}^{m-1} L_mq T_qn,   T_nn = D_n,
         // keeping T_qn in fp32 MFMA accumulators: with k = 4g + i at step i a
         // lane's accumulator element i is exactly its B operand, so no block
         // goes back through LDS.  Every block is written once, scaled by beta of
         // its column and rounded, into the MFMA operand array Tp.
+        // Q+ = scale Q Gamma as the chain's operand fragments (rows tokens, k
+        // channels in kmap order), from the row operand and exp(B_m); fragment f
+        // is token tile f / KS, k-step f % KS.
+        auto qp_frag = [&](int f) {
+            const int m = f / KS, ks = f % KS;
+            const frag_t<T> qr = load_frag_kmap<T>(&sm.ops.QR[16 * m + x][32 * ks], g);
+            const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 4 * g]);
+            const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 16 + 4 * g]);
+            frag_t<T> qp;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qp[e] = from_f<T>(to_f<T>(qr[e]) * e0[e]);
+                qp[4 + e] = from_f<T>(to_f<T>(qr[4 + e]) * e1[e]);
+            }
+            store8(blk + BL::Q_OFF + ((m * KS + ks) * 64 + l) * 8, qp);
+        };
         {
             float(*L)[SM::LP] = sm.L;
             constexpr int LP = SM::LP;
-            if (w == 0) {
-                const int mb = l >> 4, cc = l & 15, o0 = 16 * mb;
-                const float bc = sm.beta[o0 + cc];
-                float xv[16];
+            if (w < 4) {
+                // D_m = (I + N)^-1 with N = L_mm strictly lower (N^16 = 0), as the
+                // finite product (I - N)(I + N^2)(I + N^4)(I + N^8) on fp32 MFMA.
+                // A product X Y takes Y in accumulator layout and X in row layout,
+                // which is X^T in accumulator layout; so each factor is also kept
+                // transposed.  Wave m inverts block m.
+                const int o0 = 16 * w;
+                f32x4 nr, na;  // N row layout (lane (x,g): N[x][4g+i]) and accumulator layout (N[4g+i][x])
+                nr = *reinterpret_cast<const f32x4 *>(&L[o0 + x][o0 + 4 * g]);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float acc = (r == cc) ? 1.f : 0.f;
+                for (int i = 0; i < 4; ++i) na[i] = L[o0 + 4 * g + i][o0 + x];
+                auto mm = [](const f32x4 &a, const f32x4 &b) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int k2 = 0; k2 < r; ++k2) acc -= L[o0 + r][o0 + k2] * xv[k2];
-                    xv[r] = acc;
+                    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+                    return acc;
+                };
+                f32x4 a1r, a1a;  // A1 = I - N
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a1r[i] = (x == 4 * g + i ? 1.f : 0.f) - nr[i];
+                    a1a[i] = (x == 4 * g + i ? 1.f : 0.f) - na[i];
                 }
-                float *Dm = dblk(sm, mb);
+                const f32x4 n2 = mm(nr, na), n2t = mm(na, nr);
+                const f32x4 a2 = a1a + mm(a1r, n2), a2t = a1r + mm(n2, a1r);
+                const f32x4 n4 = mm(n2t, n2), n4t = mm(n2, n2t);
+                const f32x4 a3 = a2 + mm(a2t, n4), a3t = a2t + mm(n4, a2t);
+                const f32x4 n8 = mm(n4t, n4);
+                const f32x4 dmv = a3 + mm(a3t, n8);  // D[4g+i][x]
+                const float bc = sm.beta[o0 + x];
+                float *Dm = dblk(sm, w);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    Dm[r * LP + cc] = xv[r];
-                    sm.y.t.Tp[o0 + r][o0 + cc] = from_f<T>(xv[r] * bc);
+                for (int i = 0; i < 4; ++i) {
+                    Dm[(4 * g + i) * LP + x] = dmv[i];
+                    sm.y.t.Tp[o0 + 4 * g + i][o0 + x] = from_f<T>(dmv[i] * bc);
                 }
             } else {
-                for (int e = t - 64; e < 6 * 256; e += 64 * (IWAVES - 1)) {  // upper off-diagonal blocks are zero
+                for (int e = t - 256; e < 6 * 256; e += 64 * (IWAVES - 4)) {  // upper off-diagonal blocks are zero
                     const int bi = e / 256, a = (e / 16) % 16, b = e % 16;
                     const int mb = (bi < 3) ? 0 : (bi < 5 ? 1 : 2);
                     const int nb = (bi < 3) ? bi + 1 : (bi < 5 ? bi - 1 : 3);
                     sm.y.t.Tp[16 * mb + a][16 * nb + b] = from_f<T>(0.f);
                 }
-                // Q+ = scale Q Gamma as the chain's operand fragments (rows tokens, k
-                // channels in kmap order), from the row operand and exp(B_m).
-                for (int f = w - 1; f < 4 * KS; f += IWAVES - 1) {
-                    const int m = f / KS, ks = f % KS;
-                    const frag_t<T> qr = load_frag_kmap<T>(&sm.ops.QR[16 * m + x][32 * ks], g);
-                    const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 4 * g]);
-                    const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 16 + 4 * g]);
-                    frag_t<T> qp;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        qp[e] = from_f<T>(to_f<T>(qr[e]) * e0[e]);
-                        qp[4 + e] = from_f<T>(to_f<T>(qr[4 + e]) * e1[e]);
-                    }
-                    store8(blk + BL::Q_OFF + ((m * KS + ks) * 64 + l) * 8, qp);
-                }
+                for (int f = w - 4; f < 2 * KS; f += IWAVES - 4) qp_frag(f);  // first half of Q+
             }
             lds_barrier();
             if (w < 3) {
@@ -574,6 +595,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     const int R = f / 2, ks = f % 2;
                     store8(blk + BL::KT_OFF + (f * 64 + l) * 8, load_frag_kmap<T>(&sm.KtT[16 * R + x][32 * ks], g));
                 }
+                for (int f = 2 * KS + w - 3; f < 4 * KS; f += IWAVES - 3) qp_frag(f);  // second half of Q+
             }
         }
         lds_barrier();
