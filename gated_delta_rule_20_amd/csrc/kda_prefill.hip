@@ -347,12 +347,6 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             for (int cc = 0; cc < CPT; ++cc) sm.tot[2 * m0 + hf][ch0 + cc] = run[cc];
             if (l < HT) sm.beta[tb + l] = to_f<T>(raw.beta);
         }
-#pragma unroll
-        for (int r = 0; r < HT; ++r) {
-            bool ok;
-            const size_t row = nrow(r, ok);
-            raw.g[r] = ok ? *reinterpret_cast<const ku *>(ng + row * DK + ch0) : zk;
-        }
         {
             const int bt = tb + l;
             raw.beta = (have2 && l < HT && bt < len2) ? ((const T *)p.beta)[(size_t)(tok2 + bt) * p.H + h2] : from_f<T>(0.f);
@@ -417,6 +411,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 {
                     bool ok;
                     const size_t row = nrow(r0, ok);
+                    raw.g[r0] = ok ? *reinterpret_cast<const ku *>(ng + row * DK + ch0) : zk;
                     raw.k[r0] = ok ? *reinterpret_cast<const ku *>(nk + row * DK + ch0) : zk;
                     raw.q[r0] = ok ? *reinterpret_cast<const ku *>(nq + row * DK + ch0) : zk;
                 }
