@@ -624,17 +624,30 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 }
 
 // -----------------------------------------------------------------------------
-// Chain stage: one workgroup (4 waves) per (sequence, head, 16-column slice).
+// Chain stage: one workgroup per (sequence, head, 16-column slice of d_v);
+// columns of S evolve independently (V~ = U - W S acts column by column).
 // Workgroup ids are dispatched round-robin over the 8 XCDs (id % 8), so the NS
 // slices of one (sequence, head) are given ids congruent mod 8: they share an
-// XCD and read the chunk blocks through one L2.  The operand fragments of the
-// next two chunks are in flight while the current chunk is computed.
+// XCD and read the chunk blocks through one L2.
+//
+// Eight waves in two roles over the same four token tiles (wave w, tile
+// w % 4): waves 0-3 carry the recurrence (S in fp32 registers, rows
+// 16*RT*w .. 16*RT*(w+1)-1; V~ = U - W S and S <- gamma^C S + K~^T V~), waves
+// 4-7 form the output (O^T = S^T (Q+)^T + V~^T A^T) from the S^T and V~^T
+// that the recurrence waves exchange through LDS.  Each role loads only its
+// own operands, straight into registers, one chunk ahead, spread between its
+// MFMA groups: a wave whose vector load is not accepted stalls in order, and
+// the two roles sharing a SIMD keep it busy while the other waits.
 // -----------------------------------------------------------------------------
-template <typename T, int DK> struct ChainFrags {
+template <typename T, int DK> struct ChainRec {   // recurrence operands of one chunk
     static constexpr int KS = DK / 32, RT = DK / 64;
-    frag_t<T> Wn[KS], Qp[KS], Af[2], Kt[RT][2];
+    frag_t<T> Wn[KS], Kt[RT][2];
     quad_t<T> U;
     f32x4 gam[RT];
+};
+template <typename T, int DK> struct ChainOut {   // output operands of one chunk
+    static constexpr int KS = DK / 32;
+    frag_t<T> Qp[KS], Af[2];
 };
 
 // Fragment with every bit ANDed with m (m = 0 or ~0): a branch-free zeroing.
@@ -646,8 +659,7 @@ template <typename T> __device__ __forceinline__ frag_t<T> mask_frag(frag_t<T> f
     return __builtin_bit_cast(frag_t<T>, u);
 }
 
-// Loads of one chunk's operands for wave wv, in four parts so that they can be
-// spread over the previous chunk's computation.  `b` is the block (uniform);
+// Loads of one chunk's operands for tile wv.  `b` is the block (uniform);
 // each access is scalar base + lane offset + immediate.
 template <typename V> __device__ __forceinline__ V ldg(const char *b, size_t off, uint32_t lane_off)
 {
@@ -658,24 +670,13 @@ template <typename T, int DK, int DV> struct ChainLoad {
     using BL = Block<T, DK, DV>;
     static constexpr int KS = DK / 32, RT = DK / 64;
     static constexpr size_t FB = sizeof(frag_t<T>), QB = sizeof(quad_t<T>);
-    __device__ static __forceinline__ void w(ChainFrags<T, DK> &f, const char *b, int wv, int l, int sl) {
+    __device__ static __forceinline__ void uw(ChainRec<T, DK> &f, const char *b, int wv, int l, int sl) {
         f.U = ldg<quad_t<T>>(b, BL::U_OFF * sizeof(T) + (size_t)(sl * 4 + wv) * 64 * QB, (uint32_t)l * QB);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             f.Wn[ks] = ldg<frag_t<T>>(b, BL::W_OFF * sizeof(T) + (size_t)(wv * KS + ks) * 64 * FB, (uint32_t)l * FB);
     }
-    __device__ static __forceinline__ void q(ChainFrags<T, DK> &f, const char *b, int wv, int l) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            f.Qp[ks] = ldg<frag_t<T>>(b, BL::Q_OFF * sizeof(T) + (size_t)(wv * KS + ks) * 64 * FB, (uint32_t)l * FB);
-    }
-    __device__ static __forceinline__ void a(ChainFrags<T, DK> &f, const char *b, int wv, int l) {
-        // Waves 0, 1 have no second k-step of A (all zero, not stored): they load
-        // the first one again and the step masks it to zero.
-        f.Af[0] = ldg<frag_t<T>>(b, BL::A_OFF * sizeof(T) + (size_t)(wv * 2) * 64 * FB, (uint32_t)l * FB);
-        f.Af[1] = ldg<frag_t<T>>(b, BL::A_OFF * sizeof(T) + (size_t)(wv * 2 + (wv >= 2)) * 64 * FB, (uint32_t)l * FB);
-    }
-    __device__ static __forceinline__ void kt(ChainFrags<T, DK> &f, const char *b, int wv, int l, int g) {
+    __device__ static __forceinline__ void kt(ChainRec<T, DK> &f, const char *b, int wv, int l, int g) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
@@ -685,15 +686,47 @@ template <typename T, int DK, int DV> struct ChainLoad {
             f.gam[rt] = ldg<f32x4>(b, BL::GAMMA_BYTE + (size_t)(wv * RT + rt) * 64, (uint32_t)g * 16u);
         }
     }
-    __device__ static __forceinline__ void all(ChainFrags<T, DK> &f, const char *b, int wv, int l, int g, int sl) {
-        w(f, b, wv, l, sl); q(f, b, wv, l); a(f, b, wv, l); kt(f, b, wv, l, g);
+    __device__ static __forceinline__ void q(ChainOut<T, DK> &f, const char *b, int wv, int l) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            f.Qp[ks] = ldg<frag_t<T>>(b, BL::Q_OFF * sizeof(T) + (size_t)(wv * KS + ks) * 64 * FB, (uint32_t)l * FB);
+    }
+    __device__ static __forceinline__ void a(ChainOut<T, DK> &f, const char *b, int wv, int l) {
+        // Tiles 0, 1 have no second k-step of A (all zero, not stored): they load
+        // the first one again and the step masks it to zero.
+        f.Af[0] = ldg<frag_t<T>>(b, BL::A_OFF * sizeof(T) + (size_t)(wv * 2) * 64 * FB, (uint32_t)l * FB);
+        f.Af[1] = ldg<frag_t<T>>(b, BL::A_OFF * sizeof(T) + (size_t)(wv * 2 + (wv >= 2)) * 64 * FB, (uint32_t)l * FB);
     }
 };
 
+// Runs step(cur, lc, next, lc + 1) over lc = 0 .. nch-1 with two alternating
+// operand buffers.  The first one or two chunks are peeled so that the loop
+// body holds exactly two steps with no branch between them (which keeps the
+// compiler's load waits one chunk deep).
+template <typename F, typename Step>
+__device__ __forceinline__ void run_chunks(int nch, F &fa, F &fb, Step &&step)
+{
+    if (nch <= 0) return;
+    step(fa, 0, fb, 1);
+    if (nch & 1) {
+        for (int lc = 1; lc < nch; lc += 2) {
+            step(fb, lc, fa, lc + 1);
+            step(fa, lc + 1, fb, lc + 2);
+        }
+    } else {
+        step(fb, 1, fa, 2);
+        for (int lc = 2; lc < nch; lc += 2) {
+            step(fa, lc, fb, lc + 1);
+            step(fb, lc + 1, fa, lc + 2);
+        }
+    }
+}
+
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void chain_kernel(PrefillParams p)
+__global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
 {
     using BL = Block<T, DK, DV>;
+    using LD = ChainLoad<T, DK, DV>;
     constexpr int KS = DK / 32, RT = DK / 64, NS = DV / 16;
     constexpr int PS = DK + 8, PV = CHUNK + 8;
     // S^T and V~^T slices, [column][k], with k stored in kmap order inside each
@@ -721,103 +754,111 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p)
         nch = (p.T + CHUNK - 1) / CHUNK;
         chunk0 = s * nch;
     }
-    const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 4, x = l & 15;
+    const int t = threadIdx.x, wr = __builtin_amdgcn_readfirstlane(t >> 6), w = wr & 3;
+    const int l = t & 63, g = l >> 4, x = l & 15;
     const int col = 16 * sl + x;
-    const uint32_t amask = (w >= 2) ? ~0u : 0u;
-
-    // state slice in accumulator layout: rows 16*(w*RT+rt) + 4g + i, column col
-    f32x4 S[RT];
     const size_t sbase = ((size_t)s * p.H + h) * DK * DV;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * (w * RT + rt) + 4 * g + i;
-            S[rt][i] = p.h0 ? p.h0[sbase + (size_t)row * DV + col] : 0.f;
-        }
-        *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
-    }
-
     const char *blk0 = p.blocks + ((size_t)h * p.n_chunks_cap + chunk0) * BL::BYTES;
-    T *o = (T *)p.o;
-    using LD = ChainLoad<T, DK, DV>;
-    // One chunk of the recurrence with operands f (already in registers); the
-    // operands of chunk nlc are loaded into nx in four parts placed between
-    // the MFMA groups, so that the wave does not stall on one burst of loads.
-    auto step = [&](const ChainFrags<T, DK> &f, int lc, ChainFrags<T, DK> &nx, int nlc) {
-        const char *nb = blk0 + (size_t)min(nlc, nch - 1) * BL::BYTES;  // last block again at the end
-        lds_barrier();  // S^T of this chunk's entering state is in LDS
-        frag_t<T> Sk[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) Sk[ks] = load_frag_lin<T>(&sST[x][32 * ks], g);
-        f32x4 accV = quad_to_f<T>(f.U), accO = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) accV = mma(f.Wn[ks], Sk[ks], accV);  // V~ = U - W S
-        __builtin_amdgcn_sched_barrier(0);
-        LD::w(nx, nb, w, l, sl);
-        __builtin_amdgcn_sched_barrier(0);
-        // The output is formed transposed, O^T = S^T (Gamma Q)^T + V~^T A^T: the same
-        // fragments with the operand roles swapped, so each lane ends with four
-        // consecutive columns of one token (one 8-byte store).
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) accO = mma(Sk[ks], f.Qp[ks], accO);
-        *reinterpret_cast<quad_t<T> *>(&sVT[x][kpos(16 * w + 4 * g)]) = make_quad<T>(accV);
-        __builtin_amdgcn_sched_barrier(0);
-        LD::q(nx, nb, w, l);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();  // V~ of the whole chunk is in LDS
-        frag_t<T> Vf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) Vf[ks] = load_frag_lin<T>(&sVT[x][32 * ks], g);
-        accO = mma(Vf[0], f.Af[0], accO);             // + (A V~)^T
-        accO = mma(Vf[1], mask_frag<T>(f.Af[1], amask), accO);
+    auto blk = [&](int lc) { return blk0 + (size_t)min(lc, nch - 1) * BL::BYTES; };  // last block again at the end
+
+    if (wr < 4) {
+        // ---- recurrence waves ------------------------------------------------
+        // state slice in accumulator layout: rows 16*(w*RT+rt) + 4g + i, column col
+        f32x4 S[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            S[rt] *= f.gam[rt];                       // Diag(gamma^C) S
-            S[rt] = mma(f.Kt[rt][0], Vf[0], S[rt]);   // + (K gamma^C / Gamma)^T V~
-            S[rt] = mma(f.Kt[rt][1], Vf[1], S[rt]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        LD::a(nx, nb, w, l);
-        LD::kt(nx, nb, w, l, g);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
-        const int clen = min(CHUNK, len - lc * CHUNK), r = 16 * w + x;
-        if (r < clen)
-            *reinterpret_cast<quad_t<T> *>(o + ((size_t)(tok0 + lc * CHUNK + r) * p.H + h) * DV + 16 * sl + 4 * g) =
-                make_quad<T>(accO);
-    };
-    // Two operand buffers alternate (chunk indices past the end are clamped: a
-    // repeated load is harmless).  The first one or two chunks are peeled so
-    // that the loop body holds exactly two steps with no branch between them
-    // (which keeps the compiler's load waits one chunk deep).
-    ChainFrags<T, DK> fa, fb;
-    if (nch > 0) {
-        LD::all(fa, blk0, w, l, g, sl);
-        step(fa, 0, fb, 1);
-        if (nch & 1) {
-            for (int lc = 1; lc < nch; lc += 2) {
-                step(fb, lc, fa, lc + 1);
-                step(fa, lc + 1, fb, lc + 2);
-            }
-        } else {
-            step(fb, 1, fa, 2);
-            for (int lc = 2; lc < nch; lc += 2) {
-                step(fa, lc, fb, lc + 1);
-                step(fb, lc + 1, fa, lc + 2);
-            }
-        }
-    }
-    if (p.hT) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * (w * RT + rt) + 4 * g + i;
-                p.hT[sbase + (size_t)row * DV + col] = S[rt][i];
+                S[rt][i] = p.h0 ? p.h0[sbase + (size_t)row * DV + col] : 0.f;
             }
+            *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
+        }
+        auto step = [&](const ChainRec<T, DK> &f, int lc, ChainRec<T, DK> &nx, int nlc) {
+            (void)lc;
+            const char *nb = blk(nlc);
+            lds_barrier();  // S^T of this chunk's entering state is in LDS
+            frag_t<T> Sk[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) Sk[ks] = load_frag_lin<T>(&sST[x][32 * ks], g);
+            f32x4 accV = quad_to_f<T>(f.U);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) accV = mma(f.Wn[ks], Sk[ks], accV);  // V~ = U - W S
+            __builtin_amdgcn_sched_barrier(0);
+            LD::uw(nx, nb, w, l, sl);
+            __builtin_amdgcn_sched_barrier(0);
+            *reinterpret_cast<quad_t<T> *>(&sVT[x][kpos(16 * w + 4 * g)]) = make_quad<T>(accV);
+            lds_barrier();  // V~ of the whole chunk is in LDS; S^T fully read
+            frag_t<T> Vf[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) Vf[ks] = load_frag_lin<T>(&sVT[x][32 * ks], g);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                S[rt] *= f.gam[rt];                       // Diag(gamma^C) S
+                S[rt] = mma(f.Kt[rt][0], Vf[0], S[rt]);   // + (K gamma^C / Gamma)^T V~
+                S[rt] = mma(f.Kt[rt][1], Vf[1], S[rt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            LD::kt(nx, nb, w, l, g);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
+        };
+        ChainRec<T, DK> fa, fb;
+        if (nch > 0) {
+            LD::uw(fa, blk0, w, l, sl);
+            LD::kt(fa, blk0, w, l, g);
+        }
+        run_chunks(nch, fa, fb, step);
+        if (p.hT) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * (w * RT + rt) + 4 * g + i;
+                    p.hT[sbase + (size_t)row * DV + col] = S[rt][i];
+                }
+        }
+    } else {
+        // ---- output waves ------------------------------------------------------
+        const uint32_t amask = (w >= 2) ? ~0u : 0u;
+        T *o = (T *)p.o;
+        auto step = [&](const ChainOut<T, DK> &f, int lc, ChainOut<T, DK> &nx, int nlc) {
+            const char *nb = blk(nlc);
+            lds_barrier();  // S^T of this chunk's entering state is in LDS
+            frag_t<T> Sk[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) Sk[ks] = load_frag_lin<T>(&sST[x][32 * ks], g);
+            // The output is formed transposed, O^T = S^T (Gamma Q)^T + V~^T A^T: the same
+            // fragments with the operand roles swapped, so each lane ends with four
+            // consecutive columns of one token (one 8-byte store).
+            f32x4 accO = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) accO = mma(Sk[ks], f.Qp[ks], accO);
+            __builtin_amdgcn_sched_barrier(0);
+            LD::q(nx, nb, w, l);
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();  // V~ of the whole chunk is in LDS
+            frag_t<T> Vf[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) Vf[ks] = load_frag_lin<T>(&sVT[x][32 * ks], g);
+            accO = mma(Vf[0], f.Af[0], accO);             // + (A V~)^T
+            accO = mma(Vf[1], mask_frag<T>(f.Af[1], amask), accO);
+            __builtin_amdgcn_sched_barrier(0);
+            LD::a(nx, nb, w, l);
+            __builtin_amdgcn_sched_barrier(0);
+            const int clen = min(CHUNK, len - lc * CHUNK), r = 16 * w + x;
+            if (r < clen)
+                *reinterpret_cast<quad_t<T> *>(o + ((size_t)(tok0 + lc * CHUNK + r) * p.H + h) * DV + 16 * sl + 4 * g) =
+                    make_quad<T>(accO);
+        };
+        ChainOut<T, DK> fa, fb;
+        if (nch > 0) {
+            LD::q(fa, blk0, w, l);
+            LD::a(fa, blk0, w, l);
+        }
+        run_chunks(nch, fa, fb, step);
     }
 }
 
@@ -853,7 +894,7 @@ static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
     }
     const long npairs = (long)p.N * p.H;
     const unsigned grid = (unsigned)(((npairs + 7) / 8) * 8 * (DV / 16));
-    if (grid > 0) hipLaunchKernelGGL((chain_kernel<T, DK, DV>), dim3(grid), dim3(256), 0, st, p);
+    if (grid > 0) hipLaunchKernelGGL((chain_kernel<T, DK, DV>), dim3(grid), dim3(512), 0, st, p);
     return hipGetLastError();
 }
 
