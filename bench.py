@@ -22,6 +22,8 @@ import argparse
 import hashlib
 import json
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -112,8 +114,8 @@ def bench_prefill(steps, warmup, n_sets=3):
     Dv = sets[0][0]["v"].shape[-1]
     nbytes, flops = prefill_counts(B * T, H, Dk, Dv, B)
     ms = sum(per_call) / len(per_call)
-    return dict(ms=ms, ms_min=min(per_call), wall_ms=wall, tokens=B * T, bytes=nbytes, flops=flops,
-                inputs=sets[0][0], shape=(B, T, H, Dk, Dv))
+    return dict(ms=ms, ms_min=min(per_call), ms_median=statistics.median(per_call), wall_ms=wall, tokens=B * T,
+                bytes=nbytes, flops=flops, inputs=sets[0][0], shape=(B, T, H, Dk, Dv))
 
 
 def bench_decode(warmup_rounds=1):
@@ -137,7 +139,8 @@ def bench_decode(warmup_rounds=1):
     Dv = steps[0]["v"].shape[-1]
     nbytes, flops = decode_counts(N, H, Dk, Dv)
     us = 1e3 * sum(per_call) / len(per_call)
-    return dict(us=us, us_min=1e3 * min(per_call), steps=len(steps), N=N, H=H, bytes=nbytes, flops=flops)
+    return dict(us=us, us_min=1e3 * min(per_call), us_median=1e3 * statistics.median(per_call), steps=len(steps),
+                N=N, H=H, bytes=nbytes, flops=flops)
 
 
 def copy_calibration(steps, nbytes=1 << 30):
@@ -151,9 +154,21 @@ def copy_calibration(steps, nbytes=1 << 30):
     return {"copy_bytes_each_way": nbytes, "ms": ms, "GBps_read_plus_write": 2 * nbytes / (ms / 1e3) / 1e9}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(inp, max_threads=16):
     """The fp64 oracle on the host cores, over the full prefill_8k input set
-    (best of two runs).  Reported baseline only."""
+    (best of two runs), and on one thread over the first 2 heads.  Reported
+    baseline only."""
     import oracle
     f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()[0]
     q, k, v, z, b = (f64(inp[x]) for x in ("q", "k", "v", "z", "beta"))
@@ -167,10 +182,31 @@ def cpu_baseline(inp, max_threads=16):
                                     return_threads=True)
         dt = time.perf_counter() - t0
         best = dt if best is None else min(best, dt)
-    T = q.shape[0]
+    T, H = q.shape[0], q.shape[1]
+    h1 = 2  # one-thread run: 2 of the heads, scaled to the full workload
+    t0 = time.perf_counter()
+    oracle.forward(q[:, :h1].copy(), k[:, :h1].copy(), v[:, :h1].copy(), z[:, :h1].copy(), b[:, :h1].copy(),
+                   h0=h0[:, :h1].copy(), A_log=A[:h1].copy(), g_min=inp["g_min"], nthreads=1)
+    one = (time.perf_counter() - t0) * H / h1
     return {"value": T / best, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
-            "sample": f"full prefill_8k workload ({T} tokens x {q.shape[1]} heads), fp64, best of 2 runs, "
-                      f"{best:.2f} s"}
+            "sample": f"full prefill_8k workload ({T} tokens x {H} heads), fp64, best of 2 runs, {best:.2f} s",
+            "one_thread_tokens_per_s": T / one, "host_cpus": os.cpu_count(), "host_cpu_model": cpu_model()}
+
+
+def measured_peaks():
+    """Peaks measured on this device as references beside the published ones:
+    a bf16 GEMM at 8192^3 (torch.matmul, hipBLASLt) and a 1 GiB device copy."""
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b_ = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        torch.matmul(a, b_)
+    per_call, _ = time_calls(lambda i: torch.matmul(a, b_), 10, stream)
+    gemm_ms = statistics.median(per_call)
+    del a, b_
+    cp = copy_calibration(10)
+    return {"bf16_gemm_8192_tflops": 2 * 8192 ** 3 / (gemm_ms / 1e3) / 1e12,
+            "copy_1GiB_read_plus_write_gbs": cp["GBps_read_plus_write"]}
 
 
 def main():
@@ -180,6 +216,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured GEMM / copy reference peaks")
     ap.add_argument("--mode", choices=["all", "prefill", "decode", "copy"], default="all",
                     help="prefill/decode/copy run one part only (for profiler runs); the JSON line "
                          "of the benchmark contract is printed in mode 'all'")
@@ -231,6 +268,7 @@ def main():
         "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops": pf["flops"]},
         "prefill_ms_min": pf["ms_min"],
+        "prefill_ms_median": pf["ms_median"],
         "prefill_wall_ms": pf["wall_ms"],
     }
     if not args.no_decode:
@@ -239,12 +277,20 @@ def main():
         result["decode"] = {
             "workload": f"decode_512: N={dc['N']} x 1 token, H={dc['H']}, d=128, fp32 state 1 GiB in place, "
                         f"{dc['steps']} steps with fresh inputs",
-            "us_per_step": dc["us"], "us_min": dc["us_min"],
+            "us_per_step": dc["us"], "us_min": dc["us_min"], "us_median": dc["us_median"],
             "tokens_per_s": dc["N"] / (dc["us"] / 1e6),
             "roofline": {"bound": "hbm", "kernel": "recurrent_step_kernel", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                          "traffic": profiled_traffic("decode"), "algorithmic_bytes": dc["bytes"]},
         }
+    if not args.no_peaks:
+        pk = measured_peaks()
+        result["measured_peaks"] = pk
+        result["roofline"]["frac_of_measured_copy"] = achieved / pk["copy_1GiB_read_plus_write_gbs"]
+        result["mfma"]["frac_of_measured_gemm"] = tflops / pk["bf16_gemm_8192_tflops"]
+        if "decode" in result:
+            d = result["decode"]["roofline"]
+            d["frac_of_measured_copy"] = d["achieved"] / pk["copy_1GiB_read_plus_write_gbs"]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pf["inputs"])
     print(json.dumps(result))
