@@ -88,7 +88,9 @@ def time_calls(fn, n, stream):
     return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
 
 
-def bench_prefill(steps, warmup, n_sets=3):
+def bench_prefill(steps, warmup, n_sets=3, ckpt_every=0):
+    """prefill_8k timed per call.  ckpt_every > 0 also writes a prefix-state
+    checkpoint every ckpt_every chunks (slots for the whole sequence)."""
     w = W.WORKLOADS["prefill_8k"]
     import dataclasses
     sets = []
@@ -98,14 +100,19 @@ def bench_prefill(steps, warmup, n_sets=3):
         hT = torch.empty_like(inp["h0"])
         nws = kda.chunk_fwd_workspace_size(inp["q"], inp["v"])
         ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
-        sets.append((inp, o, hT, ws))
+        ck = None
+        if ckpt_every > 0:
+            B, T, H, Dk = inp["q"].shape
+            slots = max(1, T // (64 * ckpt_every))
+            ck = torch.empty((B, slots, H, Dk, inp["v"].shape[-1]), dtype=torch.float32, device="cuda")
+        sets.append((inp, o, hT, ws, ck))
     stream = torch.cuda.current_stream()
 
     def call(i):
-        inp, o, hT, ws = sets[i % n_sets]
+        inp, o, hT, ws, ck = sets[i % n_sets]
         kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["z"], inp["beta"], A_log=inp["A_log"],
                       g_min=inp["g_min"], initial_state=inp["h0"], out=o, final_state=hT,
-                      workspace=ws, stream=stream)
+                      workspace=ws, stream=stream, checkpoints=ck, checkpoint_every=ckpt_every)
 
     for i in range(warmup):
         call(i)
@@ -114,8 +121,12 @@ def bench_prefill(steps, warmup, n_sets=3):
     Dv = sets[0][0]["v"].shape[-1]
     nbytes, flops = prefill_counts(B * T, H, Dk, Dv, B)
     ms = sum(per_call) / len(per_call)
+    n_ck = 0
+    if ckpt_every > 0:  # slots strictly inside the sequence are written
+        n_ck = B * H * min(sets[0][4].shape[1], (T - 1) // (64 * ckpt_every))
     return dict(ms=ms, ms_min=min(per_call), ms_median=statistics.median(per_call), wall_ms=wall, tokens=B * T,
-                bytes=nbytes, flops=flops, inputs=sets[0][0], shape=(B, T, H, Dk, Dv))
+                bytes=nbytes + 4 * Dk * Dv * n_ck, flops=flops, inputs=sets[0][0], shape=(B, T, H, Dk, Dv),
+                checkpoint_states=n_ck)
 
 
 def bench_decode(warmup_rounds=1):
@@ -270,6 +281,14 @@ def main():
         "prefill_ms_min": pf["ms_min"],
         "prefill_ms_median": pf["ms_median"],
         "prefill_wall_ms": pf["wall_ms"],
+    }
+    ck = bench_prefill(args.steps, args.warmup, ckpt_every=8)
+    result["prefill_with_checkpoints"] = {
+        "workload": "prefill_8k with a prefix-state checkpoint every 8 chunks (512 tokens), fp32 slots",
+        "ms_per_step": ck["ms"], "ms_median": ck["ms_median"], "tokens_per_s": ck["tokens"] / (ck["ms"] / 1e3),
+        "checkpoint_states_written": ck["checkpoint_states"],
+        "hbm_GBps": ck["bytes"] / (ck["ms"] / 1e3) / 1e9, "algorithmic_bytes": ck["bytes"],
+        "overhead_vs_plain": ck["ms"] / pf["ms"] - 1.0,
     }
     if not args.no_decode:
         dc = bench_decode()

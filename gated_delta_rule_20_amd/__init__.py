@@ -44,7 +44,8 @@ class ChunkFwdArgs(ctypes.Structure):
                 ("cu_seqlens", ctypes.c_void_p), ("N", ctypes.c_int32),
                 ("initial_state", ctypes.c_void_p), ("o", ctypes.c_void_p),
                 ("final_state", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("checkpoints", ctypes.c_void_p),
+                ("checkpoint_every", ctypes.c_int32), ("checkpoint_slots", ctypes.c_int32)]
 
 
 class StepArgs(ctypes.Structure):
@@ -104,12 +105,24 @@ def _dev(t, name, dtype=None):
     return t
 
 
+def _same_lead(q, k, v, g, beta, A_log, H):
+    """q, k, g share one shape; v and beta share its leading axes; A_log is [H]."""
+    if k.shape != q.shape or g.shape != q.shape:
+        raise ValueError(f"k and g must have q's shape {tuple(q.shape)}, got {tuple(k.shape)}, {tuple(g.shape)}")
+    if v.shape[:-1] != q.shape[:-1] or beta.shape != q.shape[:-1]:
+        raise ValueError(f"v must be [..., Dv] and beta [...] over q's leading axes {tuple(q.shape[:-1])}, "
+                         f"got {tuple(v.shape)}, {tuple(beta.shape)}")
+    if A_log is not None and A_log.numel() != H:
+        raise ValueError(f"A_log must have H = {H} entries, got {A_log.numel()}")
+
+
 def _stream(stream, device):
     s = stream if stream is not None else torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _chunk_args(q, k, v, g, beta, A_log, g_min, scale, cu_seqlens, N, h0, o, hT, ws, ws_bytes):
+def _chunk_args(q, k, v, g, beta, A_log, g_min, scale, cu_seqlens, N, h0, o, hT, ws, ws_bytes,
+                ckpt=None, ckpt_every=0):
     if cu_seqlens is not None:
         T, H, Dk = q.shape[-3:]
         B = 1
@@ -125,6 +138,9 @@ def _chunk_args(q, k, v, g, beta, A_log, g_min, scale, cu_seqlens, N, h0, o, hT,
     a.N = int(N)
     a.initial_state, a.o, a.final_state = _ptr(h0), _ptr(o), _ptr(hT)
     a.workspace, a.workspace_bytes = _ptr(ws), int(ws_bytes)
+    a.checkpoints = _ptr(ckpt)
+    a.checkpoint_every = int(ckpt_every) if ckpt is not None else 0
+    a.checkpoint_slots = int(ckpt.shape[1]) if ckpt is not None else 0
     return a
 
 
@@ -144,7 +160,8 @@ def chunk_fwd_workspace_size(q, v, *, cu_seqlens=None, N=None) -> int:
 
 def chunk_fwd(q, k, v, g, beta, *, A_log=None, g_min: float = -5.0, scale: float = 1.0,
               cu_seqlens=None, initial_state=None, output_final_state: bool = True,
-              out=None, final_state=None, workspace=None, stream=None):
+              out=None, final_state=None, workspace=None, stream=None,
+              checkpoints=None, checkpoint_every: int = 0):
     """Chunkwise-parallel KDA forward.
 
     q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H] (bf16 or fp32).
@@ -153,6 +170,9 @@ def chunk_fwd(q, k, v, g, beta, *, A_log=None, g_min: float = -5.0, scale: float
     decay logits z when ``A_log`` ([H] fp32) is given (eq. (5) gate in-kernel).
     initial_state / final_state: [N, H, Dk, Dv] fp32 (final_state may be the
     same tensor as initial_state for in-place resume).
+    checkpoints: optional [N, slots, H, Dk, Dv] fp32; slot j receives the state
+    after (j + 1) * checkpoint_every * 64 tokens of each sequence when that
+    position lies strictly inside it (other slots are left as they are).
     Returns (o, final_state or None).
     """
     lib = load_library()
@@ -170,18 +190,32 @@ def chunk_fwd(q, k, v, g, beta, *, A_log=None, g_min: float = -5.0, scale: float
         N = q.shape[0]
         H, Dk = q.shape[2], q.shape[3]
     Dv = v.shape[-1]
+    _same_lead(q, k, v, g, beta, A_log, H)
     if out is None:
         out = torch.empty(v.shape, dtype=q.dtype, device=q.device)
     _dev(out, "out", q.dtype)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
     _dev(final_state, "final_state", torch.float32)
+    _dev(checkpoints, "checkpoints", torch.float32)
+    # The C ABI takes bare pointers: sizes are checked here, before the launch.
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and tuple(t.shape) != (N, H, Dk, Dv):
+            raise ValueError(f"{name} must be [N, H, Dk, Dv] = {(N, H, Dk, Dv)}, got {tuple(t.shape)}")
+    if out.shape != v.shape:
+        raise ValueError(f"out must have v's shape {tuple(v.shape)}, got {tuple(out.shape)}")
+    if checkpoints is not None:
+        if (checkpoints.dim() != 5 or checkpoints.shape[0] != N or checkpoints.shape[1] < 1
+                or tuple(checkpoints.shape[2:]) != (H, Dk, Dv) or checkpoint_every < 1):
+            raise ValueError(f"checkpoints must be [N, slots >= 1, H, Dk, Dv] with N, H, Dk, Dv = "
+                             f"{(N, H, Dk, Dv)} and checkpoint_every >= 1; got {tuple(checkpoints.shape)}, "
+                             f"every={checkpoint_every}")
     need = chunk_fwd_workspace_size(q, v, cu_seqlens=cu_seqlens, N=N)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a = _chunk_args(q, k, v, g, beta, A_log, g_min, scale, cu_seqlens, N, initial_state,
-                    out, final_state, workspace, ws_bytes)
+                    out, final_state, workspace, ws_bytes, checkpoints, checkpoint_every)
     _check(lib, "kda_chunk_fwd", lib.kda_chunk_fwd(ctypes.byref(a), _stream(stream, q.device)))
     return out, final_state
 
@@ -197,11 +231,18 @@ def recurrent_step(q, k, v, g, beta, state, *, A_log=None, g_min: float = -5.0,
         _dev(t, name, q.dtype)
     _dev(state, "state", torch.float32)
     _dev(A_log, "A_log", torch.float32)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [N, H, Dk], got {tuple(q.shape)}")
     N, H, Dk = q.shape
     Dv = v.shape[-1]
+    _same_lead(q, k, v, g, beta, A_log, H)
+    if tuple(state.shape) != (N, H, Dk, Dv):
+        raise ValueError(f"state must be [N, H, Dk, Dv] = {(N, H, Dk, Dv)}, got {tuple(state.shape)}")
     if out is None:
         out = torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
     _dev(out, "out", q.dtype)
+    if out.shape != v.shape:
+        raise ValueError(f"out must have v's shape {tuple(v.shape)}, got {tuple(out.shape)}")
     a = StepArgs()
     a.N, a.H, a.Dk, a.Dv, a.dtype = N, H, Dk, Dv, _DTYPES[q.dtype]
     a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))

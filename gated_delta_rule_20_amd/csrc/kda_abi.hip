@@ -128,6 +128,12 @@ kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *a, void *stream)
         return fail(KDA_ERROR_INVALID_VALUE, "initial_state is not 16-byte aligned");
     if (a->final_state && !aligned16(a->final_state))
         return fail(KDA_ERROR_INVALID_VALUE, "final_state is not 16-byte aligned");
+    if (a->checkpoints) {
+        if (!aligned16(a->checkpoints)) return fail(KDA_ERROR_INVALID_VALUE, "checkpoints is not 16-byte aligned");
+        if (a->checkpoint_every < 1 || a->checkpoint_slots < 1)
+            return fail(KDA_ERROR_INVALID_VALUE, "need checkpoint_every >= 1 and checkpoint_slots >= 1 (got %d, %d)",
+                        a->checkpoint_every, a->checkpoint_slots);
+    }
     if (pl.total > 0) {
         if (!a->workspace) return fail(KDA_ERROR_WORKSPACE, "workspace is NULL but %zu bytes are needed", pl.total);
         if (a->workspace_bytes < pl.total)
@@ -149,6 +155,9 @@ kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *a, void *stream)
     p.order = pl.varlen ? (int32_t *)ws + (pl.N + 1) : nullptr;
     p.blocks = ws ? ws + pl.table : nullptr;
     p.n_chunks_cap = has_tokens ? pl.n_chunks_cap : 0;
+    p.ckpt = a->checkpoints;
+    p.ckpt_every = a->checkpoints ? a->checkpoint_every : 0;
+    p.ckpt_slots = a->checkpoints ? a->checkpoint_slots : 0;
     const hipError_t e = kda::launch_chunk_fwd(a->dtype == KDA_BF16, a->Dk, a->Dv, p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     g_err[0] = 0;

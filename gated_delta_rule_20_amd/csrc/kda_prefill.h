@@ -22,6 +22,8 @@ struct PrefillParams {
     int32_t *order;                     // [N]   (varlen; workspace)
     char *blocks;                       // [H][n_chunks_cap] per-chunk blocks (workspace)
     int n_chunks_cap;
+    float *ckpt;                        // [N, ckpt_slots, H, Dk, Dv] or null
+    int ckpt_every, ckpt_slots;         // chunks between checkpoints, slots per sequence
 };
 
 // Bytes of one (head, chunk) workspace block; 0 if the combination is unsupported.

@@ -775,7 +775,6 @@ __global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
             *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
         }
         auto step = [&](const ChainRec<T, DK> &f, int lc, ChainRec<T, DK> &nx, int nlc) {
-            (void)lc;
             const char *nb = blk(nlc);
             lds_barrier();  // S^T of this chunk's entering state is in LDS
             frag_t<T> Sk[KS];
@@ -804,6 +803,17 @@ __global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
                 *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
+            // Prefix-state checkpoint after every ckpt_every-th chunk strictly inside the sequence.
+            if (p.ckpt_every > 0 && (lc + 1) % p.ckpt_every == 0) {
+                const int j = (lc + 1) / p.ckpt_every - 1;
+                if (j < p.ckpt_slots && (lc + 1) * CHUNK < len) {
+                    float *cp = p.ckpt + (((size_t)s * p.ckpt_slots + j) * p.H + h) * DK * DV;
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) cp[(size_t)(16 * (w * RT + rt) + 4 * g + i) * DV + col] = S[rt][i];
+                }
+            }
         };
         ChainRec<T, DK> fa, fb;
         if (nch > 0) {

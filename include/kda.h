@@ -86,6 +86,20 @@ typedef enum {
  * The workspace (device memory, >= kda_chunk_fwd_workspace_size bytes,
  * 256-byte aligned) holds per-chunk intermediates; its contents on entry are
  * ignored and on exit are unspecified.
+ *
+ * State checkpoints ("Kimi K3 Technical Report", §5.4.1: the KDA state is
+ * persisted at hash-block-aligned prefix positions so that a later request
+ * sharing the prefix resumes from it):
+ *   checkpoints : [N, checkpoint_slots, H, Dk, Dv] float32, or NULL for none.
+ *   Slot j of sequence s receives the state after the first
+ *   (j + 1) * checkpoint_every * KDA_CHUNK tokens of s, for every j with that
+ *   position strictly inside the sequence and j < checkpoint_slots; other
+ *   slots are not written.  (The state after the last token is final_state.)
+ *   Resuming = passing a slot as initial_state for the remaining tokens.
+ *   checkpoint_every >= 1 and checkpoint_slots >= 1 are required when
+ *   checkpoints is set; both are ignored otherwise.  The buffer is owned by
+ *   the caller, must be 16-byte aligned and must not overlap any other
+ *   argument; its size is not checked (the library holds no shapes of it).
  */
 typedef struct {
     int32_t B, T, H, Dk, Dv;
@@ -101,6 +115,9 @@ typedef struct {
     float *final_state;
     void *workspace;
     size_t workspace_bytes;
+    float *checkpoints;            /* optional prefix-state checkpoints, see above */
+    int32_t checkpoint_every;      /* chunks of KDA_CHUNK tokens between checkpoints */
+    int32_t checkpoint_slots;      /* capacity per sequence */
 } kda_chunk_fwd_args_t;
 
 /* Workspace bytes kda_chunk_fwd needs for these shapes (pointers are not read).

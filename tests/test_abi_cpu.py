@@ -102,6 +102,9 @@ def test_workspace_size_rejects(lib, over, status, msg):
     (dict(workspace=None, workspace_bytes=0), 3, "workspace is NULL"),
     (dict(workspace=0x100000, workspace_bytes=1024), 3, "needs"),
     (dict(workspace=0x100010, workspace_bytes=1 << 30), 3, "256-byte"),
+    (dict(checkpoints=0x100008), 1, "checkpoints is not 16-byte aligned"),
+    (dict(checkpoints=0x100000, checkpoint_every=0, checkpoint_slots=4), 1, "checkpoint_every >= 1"),
+    (dict(checkpoints=0x100000, checkpoint_every=8, checkpoint_slots=0), 1, "checkpoint_slots >= 1"),
 ])
 def test_chunk_fwd_rejects_before_launch(lib, over, status, msg):
     a = _args(**over)
@@ -164,3 +167,19 @@ def test_bench_traffic_records_parse():
         t = bench.profiled_traffic(name)
         assert t is None or (isinstance(t, int) and t > 0)
     assert bench.profiled_traffic("no-such-kernel") is None
+
+
+def test_binding_shape_checks():
+    """The binding rejects mismatched operand shapes before any launch."""
+    import torch
+    from gated_delta_rule_20_amd import _same_lead
+    q = torch.zeros(1, 8, 2, 64)
+    v = torch.zeros(1, 8, 2, 32)
+    b = torch.zeros(1, 8, 2)
+    _same_lead(q, q, v, q, b, torch.zeros(2), 2)
+    with pytest.raises(ValueError, match="k and g"):
+        _same_lead(q, q[:, :4], v, q, b, None, 2)
+    with pytest.raises(ValueError, match="beta"):
+        _same_lead(q, q, v, q, b[:, :4], None, 2)
+    with pytest.raises(ValueError, match="A_log"):
+        _same_lead(q, q, v, q, b, torch.zeros(3), 2)
