@@ -245,18 +245,26 @@ __device__ __forceinline__ void load_raw(RawIn<T, DK, DV> &in, const PrefillPara
     in.alog = p.A_log ? p.A_log[h] : 0.f;
 }
 
+// Uniform read of a table the kernel never writes, through the scalar cache:
+// its completion is counted apart from the vector loads and stores, so the
+// waits it needs do not also wait for outstanding result stores.
+__device__ __forceinline__ int ld_uniform(const int32_t *ptr, int i)
+{
+    return ((const __attribute__((address_space(4))) int32_t *)ptr)[i];
+}
+
 // Token range of chunk c; false if c is past the last chunk (packed tail).
 __device__ __forceinline__ bool locate_chunk(const PrefillParams &p, int c, int &tok0, int &len)
 {
     if (p.varlen) {
-        if (c >= p.chunk_off[p.N]) return false;
+        if (c >= ld_uniform(p.chunk_off, p.N)) return false;
         int lo = 0, hi = p.N - 1;  // largest s with chunk_off[s] <= c
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (p.chunk_off[mid] <= c) lo = mid; else hi = mid - 1;
+            if (ld_uniform(p.chunk_off, mid) <= c) lo = mid; else hi = mid - 1;
         }
-        tok0 = p.cu[lo] + (c - p.chunk_off[lo]) * CHUNK;
-        len = min(CHUNK, p.cu[lo + 1] - tok0);
+        tok0 = ld_uniform(p.cu, lo) + (c - ld_uniform(p.chunk_off, lo)) * CHUNK;
+        len = min(CHUNK, ld_uniform(p.cu, lo + 1) - tok0);
     } else {
         const int cps = (p.T + CHUNK - 1) / CHUNK;
         const int s = c / cps, lc = c - s * cps;
@@ -301,6 +309,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
     bool have = next_item(p, i, c, h, tok0, len);
     R raw;
     if (have) load_raw(raw, p, tok0, len, h, w, l);
+    __builtin_amdgcn_s_waitcnt(0);
 
     while (have) {
         char *blkb = p.blocks + ((size_t)h * p.n_chunks_cap + c) * BL::BYTES;
@@ -309,9 +318,8 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 
         // ---- P1: gate (eq. 5), in-tile cumsum, elementwise operands ----------
         // The raw registers were loaded during the previous item (or before the
-        // loop); wait for them once here rather than at a conservative point
-        // behind this item's first store.
-        __builtin_amdgcn_s_waitcnt(0);
+        // loop) and have been waited for in that item's P3 (see there), so no
+        // wait here holds back on the previous item's result stores.
         // The next item's raw inputs are loaded into each raw register right after
         // its last use below, so the loads issue between this item's VALU work.
         int i2 = i + gridDim.x, c2 = 0, h2 = 0, tok2 = 0, len2 = 0;
@@ -558,6 +566,12 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 for (int f = w - 4; f < 2 * KS; f += IWAVES - 4) qp_frag(f);  // first half of Q+
             }
             lds_barrier();
+            // The next item's raw inputs were loaded during P1, two phases ago; wait
+            // for them here, where the only younger memory operations are this
+            // item's early result stores.  Loads and stores share one counter, so
+            // a wait at the top of the next item would also wait for every P3/P4
+            // store.
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
             if (w < 3) {
                 const int n = w;
                 const float bc = sm.beta[16 * n + x];
