@@ -66,7 +66,10 @@ def profiled_traffic(name):
             continue
         h = hashlib.sha256()
         for f in fields["files"].split(","):
-            with open(os.path.join(ROOT, "gated_delta_rule_20_amd", "csrc", f), "rb") as fh:
+            src = os.path.join(ROOT, "gated_delta_rule_20_amd", "csrc", f)
+            if not os.path.exists(src):  # the profiled source is gone: the record is stale
+                return None
+            with open(src, "rb") as fh:
                 h.update(fh.read())
         return int(fields["traffic_bytes"]) if h.hexdigest()[:16] == fields["digest"] else None
     return None
@@ -154,6 +157,43 @@ def bench_decode(warmup_rounds=1):
                 N=N, H=H, bytes=nbytes, flops=flops)
 
 
+def spec_counts(N, H, Dk, Dv, n_replayed, T_new, elem=2):
+    """Algorithmic bytes of one replay call: the state read and written once, the
+    replayed tokens' k, g, v, beta, and the new window's q, k, g, v, beta and o."""
+    state = 2 * N * H * Dk * Dv * 4
+    replay = n_replayed * H * (2 * Dk + Dv + 1) * elem
+    new = N * T_new * H * (3 * Dk + 2 * Dv + 1) * elem
+    return state + replay + new
+
+
+def bench_spec(T_new=4, calls=None, warmup_rounds=1):
+    """decode_512_spec: one replay call per speculative step (fresh inputs per call)."""
+    w = W.WORKLOADS["decode_512_spec"]
+    d = W.make_spec_decode(w, device="cuda", T_new=T_new, calls=calls)
+    state = d["state"]
+    cl = d["calls"]
+    outs = [torch.empty_like(c["v"]) for c in cl]
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        c = cl[i]
+        kda.recurrent_replay(c["q"], c["k"], c["v"], c["z"], c["beta"], state,
+                             replay=(c["k_r"], c["v_r"], c["z_r"], c["beta_r"]), n_replay=c["n_replay"],
+                             n_commit=1, A_log=d["A_log"], g_min=d["g_min"], out=outs[i], stream=stream)
+
+    for _ in range(warmup_rounds):
+        for i in range(len(cl)):
+            call(i)
+    per_call, _ = time_calls(call, len(cl), stream)
+    N, T, H, Dk = cl[0]["q"].shape
+    Dv = cl[0]["v"].shape[-1]
+    n_rep = sum(int(c["n_replay"].sum()) for c in cl) / len(cl)
+    nbytes = spec_counts(N, H, Dk, Dv, n_rep, T)
+    us = 1e3 * sum(per_call) / len(per_call)
+    return dict(us=us, us_median=1e3 * statistics.median(per_call), us_min=1e3 * min(per_call), calls=len(cl),
+                N=N, H=H, T_new=T, T_replay=cl[0]["k_r"].shape[1], mean_replayed=n_rep / N, bytes=nbytes)
+
+
 def copy_calibration(steps, nbytes=1 << 30):
     """A plain device-to-device copy of known size (for scaling the HBM
     FETCH_SIZE / WRITE_SIZE counters: it reads and writes nbytes each)."""
@@ -228,7 +268,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured GEMM / copy reference peaks")
-    ap.add_argument("--mode", choices=["all", "prefill", "decode", "copy"], default="all",
+    ap.add_argument("--no-spec", action="store_true", help="skip the speculative-decoding replay measurement")
+    ap.add_argument("--mode", choices=["all", "prefill", "decode", "spec", "copy"], default="all",
                     help="prefill/decode/copy run one part only (for profiler runs); the JSON line "
                          "of the benchmark contract is printed in mode 'all'")
     args = ap.parse_args()
@@ -246,6 +287,9 @@ def main():
     if args.mode == "decode":
         dc = bench_decode()
         print(json.dumps({k: v for k, v in dc.items()}))
+        return
+    if args.mode == "spec":
+        print(json.dumps(bench_spec()))
         return
 
     pf = bench_prefill(args.steps, args.warmup)
@@ -298,9 +342,28 @@ def main():
                         f"{dc['steps']} steps with fresh inputs",
             "us_per_step": dc["us"], "us_min": dc["us_min"], "us_median": dc["us_median"],
             "tokens_per_s": dc["N"] / (dc["us"] / 1e6),
-            "roofline": {"bound": "hbm", "kernel": "recurrent_step_kernel", "achieved": gbs,
+            "roofline": {"bound": "hbm", "kernel": "replay_kernel (one-token window)", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                          "traffic": profiled_traffic("decode"), "algorithmic_bytes": dc["bytes"]},
+        }
+    if not args.no_spec:
+        sp = bench_spec()
+        gbs = sp["bytes"] / (sp["us"] / 1e6) / 1e9
+        window = {}
+        for tn in (1, 2, 4, 8):
+            r = bench_spec(T_new=tn, calls=8)
+            window[str(tn)] = round(r["us"], 1)
+        result["spec_decode"] = {
+            "workload": f"decode_512_spec: N={sp['N']}, H={sp['H']}, d=128, cached drafts {sp['T_replay']} "
+                        f"(mean {sp['mean_replayed']:.2f} accepted and replayed), new window {sp['T_new']} "
+                        f"(bonus + drafts), bonus committed, {sp['calls']} calls with fresh inputs",
+            "us_per_call": sp["us"], "us_median": sp["us_median"], "us_min": sp["us_min"],
+            # committed per call and sequence: the accepted drafts replayed plus the bonus token
+            "committed_tokens_per_s": sp["N"] * (sp["mean_replayed"] + 1) / (sp["us"] / 1e6),
+            "roofline": {"bound": "hbm", "kernel": "replay_kernel", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": profiled_traffic("spec"),
+                         "algorithmic_bytes": sp["bytes"]},
+            "us_per_call_by_new_window": window,
         }
     if not args.no_peaks:
         pk = measured_peaks()

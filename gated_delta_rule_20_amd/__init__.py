@@ -16,12 +16,12 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_workspace_size", "load_library",
+__all__ = ["chunk_fwd", "recurrent_step", "recurrent_replay", "chunk_fwd_workspace_size", "load_library",
            "KDAError", "LIB_PATH", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 EXPORTED_SYMBOLS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_recurrent_step",
-                    "kda_status_string", "kda_last_error_message")
+                    "kda_recurrent_replay", "kda_status_string", "kda_last_error_message")
 
 KDA_F32, KDA_BF16 = 0, 1
 _DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
@@ -57,6 +57,18 @@ class StepArgs(ctypes.Structure):
                 ("state", ctypes.c_void_p), ("o", ctypes.c_void_p)]
 
 
+class ReplayArgs(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("H", ctypes.c_int32), ("Dk", ctypes.c_int32),
+                ("Dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("T_replay", ctypes.c_int32), ("T_new", ctypes.c_int32), ("n_commit", ctypes.c_int32),
+                ("k_r", ctypes.c_void_p), ("v_r", ctypes.c_void_p), ("g_r", ctypes.c_void_p),
+                ("beta_r", ctypes.c_void_p), ("n_replay", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("g_min", ctypes.c_float), ("scale", ctypes.c_float),
+                ("state", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -74,6 +86,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_void_p]
     lib.kda_recurrent_step.restype = ctypes.c_int
+    lib.kda_recurrent_replay.argtypes = [ctypes.POINTER(ReplayArgs), ctypes.c_void_p]
+    lib.kda_recurrent_replay.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error_message.argtypes = []
@@ -250,4 +264,67 @@ def recurrent_step(q, k, v, g, beta, state, *, A_log=None, g_min: float = -5.0,
     a.g_min, a.scale = float(g_min), float(scale)
     a.state, a.o = _ptr(state), _ptr(out)
     _check(lib, "kda_recurrent_step", lib.kda_recurrent_step(ctypes.byref(a), _stream(stream, q.device)))
+    return out
+
+
+def recurrent_replay(q, k, v, g, beta, state, *, replay=None, n_replay=None, n_commit=None,
+                     A_log=None, g_min: float = -5.0, scale: float = 1.0, out=None, stream=None):
+    """Speculative-decoding step with replay, state [N, H, Dk, Dv] fp32 in place.
+
+    New window: q, k, g [N, T, H, Dk]; v [N, T, H, Dv]; beta [N, T, H] (T may be 0
+    when all are None).  ``replay``: optional cached window (k_r, v_r, g_r, beta_r)
+    of shapes [N, Tr, H, ...]; ``n_replay`` ([N] int32 on the device, or None = Tr)
+    tokens of it are replayed first, without output.  The state written back is
+    the one after the replayed tokens and the first ``n_commit`` new tokens
+    (default: all of them).  Returns o [N, T, H, Dv] (None when T = 0)."""
+    lib = load_library()
+    ref = q if q is not None else replay[0]
+    if ref.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {ref.dtype}")
+    dt = ref.dtype
+    _dev(state, "state", torch.float32)
+    _dev(A_log, "A_log", torch.float32)
+    N, H, Dk, Dv = state.shape
+    T_new = 0
+    if q is not None:
+        for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+            _dev(t, name, dt)
+        if q.dim() != 4 or q.shape[0] != N or q.shape[2:] != (H, Dk):
+            raise ValueError(f"q must be [N, T, H, Dk] with N, H, Dk = {(N, H, Dk)}, got {tuple(q.shape)}")
+        _same_lead(q, k, v, g, beta, A_log, H)
+        if v.shape[-1] != Dv:
+            raise ValueError(f"v must end in Dv = {Dv}, got {tuple(v.shape)}")
+        T_new = q.shape[1]
+        if out is None:
+            out = torch.empty(v.shape, dtype=dt, device=q.device)
+        _dev(out, "out", dt)
+        if out.shape != v.shape:
+            raise ValueError(f"out must have v's shape {tuple(v.shape)}, got {tuple(out.shape)}")
+    n_commit = T_new if n_commit is None else int(n_commit)
+    a = ReplayArgs()
+    a.N, a.H, a.Dk, a.Dv, a.dtype = N, H, Dk, Dv, _DTYPES[dt]
+    a.T_new, a.n_commit = T_new, n_commit
+    a.T_replay = 0
+    if replay is not None:
+        k_r, v_r, g_r, beta_r = replay
+        for name, t in (("k_r", k_r), ("v_r", v_r), ("g_r", g_r), ("beta_r", beta_r)):
+            _dev(t, name, dt)
+        if k_r.dim() != 4 or k_r.shape[0] != N or k_r.shape[2:] != (H, Dk):
+            raise ValueError(f"k_r must be [N, Tr, H, Dk] with N, H, Dk = {(N, H, Dk)}, got {tuple(k_r.shape)}")
+        _same_lead(k_r, k_r, v_r, g_r, beta_r, A_log, H)
+        if v_r.shape[-1] != Dv:
+            raise ValueError(f"v_r must end in Dv = {Dv}, got {tuple(v_r.shape)}")
+        a.T_replay = k_r.shape[1]
+        a.k_r, a.v_r, a.g_r, a.beta_r = (_ptr(x) for x in (k_r, v_r, g_r, beta_r))
+        _dev(n_replay, "n_replay", torch.int32)
+        if n_replay is not None and tuple(n_replay.shape) != (N,):
+            raise ValueError(f"n_replay must be [N] = [{N}], got {tuple(n_replay.shape)}")
+        a.n_replay = _ptr(n_replay)
+    if q is not None:
+        a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
+        a.o = _ptr(out)
+    a.A_log = _ptr(A_log)
+    a.g_min, a.scale = float(g_min), float(scale)
+    a.state = _ptr(state)
+    _check(lib, "kda_recurrent_replay", lib.kda_recurrent_replay(ctypes.byref(a), _stream(stream, state.device)))
     return out

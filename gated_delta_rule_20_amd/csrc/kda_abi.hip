@@ -170,7 +170,7 @@ kda_status_t kda_recurrent_step(const kda_step_args_t *a, void *stream)
     kda_status_t st = check_common(a->dtype, a->Dk, a->Dv, a->A_log, a->g_min);
     if (st != KDA_SUCCESS) return st;
     if (a->N < 0 || a->H < 1) return fail(KDA_ERROR_INVALID_VALUE, "need N >= 0, H >= 1 (got N=%d H=%d)", a->N, a->H);
-    // two workgroups per (sequence, head) must fit the launch grid
+    // one workgroup per (sequence, head) must fit the launch grid
     if ((long long)a->N * a->H > 0x3fffffffLL) return fail(KDA_ERROR_NOT_SUPPORTED, "N*H too large");
     if (a->N == 0) { g_err[0] = 0; return KDA_SUCCESS; }
     const void *req[] = {a->q, a->k, a->v, a->g, a->beta, a->state, a->o};
@@ -181,10 +181,67 @@ kda_status_t kda_recurrent_step(const kda_step_args_t *a, void *stream)
     }
     if ((uintptr_t)a->beta & (a->dtype == KDA_BF16 ? 1u : 3u))
         return fail(KDA_ERROR_INVALID_VALUE, "beta is not aligned to its element size");
-    const hipError_t e = kda::launch_recurrent_step(a->dtype == KDA_BF16, a->N, a->H, a->Dk, a->Dv, a->q, a->k,
-                                                    a->v, a->g, a->beta, a->A_log, a->g_min, a->scale, a->state,
-                                                    a->o, (hipStream_t)stream);
+    // One decode step is a one-token window of the replay kernel: no cached
+    // tokens, one new token, committed.  [N, H, D] tensors are [N, 1, H, D].
+    kda::ReplayParams p;
+    p.N = a->N; p.H = a->H;
+    p.T_replay = 0; p.T_new = 1; p.n_commit = 1;
+    p.k_r = p.v_r = p.g_r = p.beta_r = nullptr;
+    p.n_replay = nullptr;
+    p.q = a->q; p.k = a->k; p.v = a->v; p.g = a->g; p.beta = a->beta;
+    p.A_log = a->A_log; p.g_min = a->g_min; p.scale = a->scale;
+    p.state = a->state; p.o = a->o;
+    const hipError_t e = kda::launch_recurrent_replay(a->dtype == KDA_BF16, a->Dk, a->Dv, p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "kda_recurrent_step launch");
+    g_err[0] = 0;
+    return KDA_SUCCESS;
+}
+
+kda_status_t kda_recurrent_replay(const kda_replay_args_t *a, void *stream)
+{
+    if (!a) return fail(KDA_ERROR_INVALID_VALUE, "args is NULL");
+    kda_status_t st = check_common(a->dtype, a->Dk, a->Dv, a->A_log, a->g_min);
+    if (st != KDA_SUCCESS) return st;
+    if (a->N < 0 || a->H < 1) return fail(KDA_ERROR_INVALID_VALUE, "need N >= 0, H >= 1 (got N=%d H=%d)", a->N, a->H);
+    if (a->T_replay < 0 || a->T_new < 0)
+        return fail(KDA_ERROR_INVALID_VALUE, "need T_replay >= 0, T_new >= 0 (got %d, %d)", a->T_replay, a->T_new);
+    if (a->n_commit < 0 || a->n_commit > a->T_new)
+        return fail(KDA_ERROR_INVALID_VALUE, "need 0 <= n_commit <= T_new (got n_commit=%d T_new=%d)", a->n_commit, a->T_new);
+    // one workgroup per (sequence, head) must fit the launch grid
+    if ((long long)a->N * a->H > 0x3fffffffLL) return fail(KDA_ERROR_NOT_SUPPORTED, "N*H too large");
+    if (!a->state) return fail(KDA_ERROR_INVALID_VALUE, "state is NULL");
+    if (!aligned16(a->state)) return fail(KDA_ERROR_INVALID_VALUE, "state is not 16-byte aligned");
+    const unsigned el = a->dtype == KDA_BF16 ? 1u : 3u;
+    if (a->T_new > 0) {
+        const void *req[] = {a->q, a->k, a->v, a->g, a->beta, a->o};
+        const char *nm[] = {"q", "k", "v", "g", "beta", "o"};
+        for (int i = 0; i < 6; ++i) {
+            if (!req[i]) return fail(KDA_ERROR_INVALID_VALUE, "%s is NULL", nm[i]);
+            if (i != 4 && !aligned16(req[i])) return fail(KDA_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", nm[i]);
+        }
+        if ((uintptr_t)a->beta & el) return fail(KDA_ERROR_INVALID_VALUE, "beta is not aligned to its element size");
+    }
+    if (a->T_replay > 0) {
+        const void *req[] = {a->k_r, a->v_r, a->g_r, a->beta_r};
+        const char *nm[] = {"k_r", "v_r", "g_r", "beta_r"};
+        for (int i = 0; i < 4; ++i) {
+            if (!req[i]) return fail(KDA_ERROR_INVALID_VALUE, "%s is NULL", nm[i]);
+            if (i != 3 && !aligned16(req[i])) return fail(KDA_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", nm[i]);
+        }
+        if ((uintptr_t)a->beta_r & el) return fail(KDA_ERROR_INVALID_VALUE, "beta_r is not aligned to its element size");
+        if (a->n_replay && ((uintptr_t)a->n_replay & 3u)) return fail(KDA_ERROR_INVALID_VALUE, "n_replay is not 4-byte aligned");
+    }
+    if (a->N == 0 || a->T_replay + a->T_new == 0) { g_err[0] = 0; return KDA_SUCCESS; }
+    kda::ReplayParams p;
+    p.N = a->N; p.H = a->H;
+    p.T_replay = a->T_replay; p.T_new = a->T_new; p.n_commit = a->n_commit;
+    p.k_r = a->k_r; p.v_r = a->v_r; p.g_r = a->g_r; p.beta_r = a->beta_r;
+    p.n_replay = a->T_replay > 0 ? a->n_replay : nullptr;
+    p.q = a->q; p.k = a->k; p.v = a->v; p.g = a->g; p.beta = a->beta;
+    p.A_log = a->A_log; p.g_min = a->g_min; p.scale = a->scale;
+    p.state = a->state; p.o = a->o;
+    const hipError_t e = kda::launch_recurrent_replay(a->dtype == KDA_BF16, a->Dk, a->Dv, p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kda_recurrent_replay launch");
     g_err[0] = 0;
     return KDA_SUCCESS;
 }

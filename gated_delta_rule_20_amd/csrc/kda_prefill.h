@@ -39,9 +39,19 @@ inline size_t table_bytes(int varlen, int N)
 // and carved the workspace into p.chunk_off / p.order / p.blocks.
 hipError_t launch_chunk_fwd(int bf16, int Dk, int Dv, const PrefillParams &p, hipStream_t stream);
 
-hipError_t launch_recurrent_step(int bf16, int N, int H, int Dk, int Dv, const void *q,
-                                 const void *k, const void *v, const void *g, const void *beta,
-                                 const float *A_log, float g_min, float scale, float *state,
-                                 void *o, hipStream_t stream);
+// Speculative-decoding step with replay (one pass over the in-place state).
+struct ReplayParams {
+    int N, H, T_replay, T_new, n_commit;
+    const void *k_r, *v_r, *g_r, *beta_r;   // cached window [N, T_replay, H, D]
+    const int32_t *n_replay;                // [N] or null (= T_replay)
+    const void *q, *k, *v, *g, *beta;       // new window [N, T_new, H, D]
+    const float *A_log;
+    float g_min, scale;
+    float *state;                           // [N, H, Dk, Dv]
+    void *o;                                // [N, T_new, H, Dv]
+};
+
+hipError_t launch_recurrent_replay(int bf16, int Dk, int Dv, const ReplayParams &p, hipStream_t stream);
+
 
 }  // namespace kda

@@ -1,0 +1,251 @@
+// kda_replay.hip -- decode-side recurrence with the state updated in place:
+// the single decode step and the speculative-decoding step with replay.
+//
+// "Kimi K3 Technical Report: Open Frontier Intelligence", §5.4.2 ("KDA"): decode
+// is bound by moving the in-place state; under speculative decoding the
+// accepted part of a draft window is rebuilt on chip from the drafts' cached
+// projected inputs, and the replayed tokens, the certain (bonus) token and the
+// next draft window run through one recurrence loop that reads the state once
+// and writes it back once, after the last token whose state is kept.  A single
+// decode step is the window with no cached tokens and one new token.
+//
+// Per token the update is eq. (1) with the eq. (5) gate, arranged as in the
+// single-step kernel (D := Diag(alpha)):
+//   p = (D S)^T k,  r = (D S)^T q,  delta = beta (v - p),
+//   S <- D S + k delta^T,  o = scale * (r + delta * (k . q)).
+// Replayed tokens skip q, r and o.
+//
+// Layout: see replay_kernel.  The state is read once at the start and written
+// once, at the commit point, each access a row of d_v consecutive floats across
+// the workgroup.
+#include "kda_common.h"
+#include "kda_prefill.h"
+
+namespace kda {
+
+// One workgroup per (sequence, head).  Each state column is held by NH = d_k/64
+// lanes of one wave (lanes l and l + 32 when NH = 2), each with 64 rows of it
+// in registers.  A token's two reductions over the rows, p = (D S)^T k and
+// r = (D S)^T q, are then sums inside each lane plus one lane swap, so the
+// token loop needs no barrier; the per-row operands are read from LDS as
+// broadcasts, four rows per read.  Token inputs are staged TB tokens at a time
+// (all loads in flight together); TB = 1 is the single decode step.
+//
+// Decay folding.  Inside a block the registers hold the state in a scaled
+// frame, X = S / P_j with P_j the per-row product of alpha over the block's
+// first j tokens (P <= 1, and P >= e^{-5 TB} by the gate's lower bound, so
+// 1/P stays far inside fp32).  In that frame one token is
+//   p = X^T (P_j k),  r = X^T (P_j q),  X <- X + (k / P_j) delta^T,
+// with P_j k, P_j q and k / P_j formed once per row during staging, so the
+// per-element decay multiply disappears; the true state X * P is formed only
+// for the write-back and at the end of a block.
+template <typename T, int DK, int DV, int TB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void replay_kernel(ReplayParams p)
+{
+    constexpr int NH = DK / 64;         // lanes per column
+    constexpr int RH = 64;              // rows per lane
+    constexpr int CPW = 64 / NH;        // columns per wave
+    constexpr int NT = DV * NH;         // threads
+    constexpr int NW = NT / 64;         // waves
+    static_assert(NH * RH == DK && NT % 64 == 0 && NT <= 256, "shape");
+    __shared__ __align__(16) float s_kd[TB][DK], s_qd[TB][DK], s_ki[TB][DK];  // P_j k, P_j q, k / P_j
+    __shared__ __align__(16) float s_pc[DK], s_pe[DK];    // P at the commit token, P at the block end
+    __shared__ float s_v[TB][DV], s_b[TB], s_kqw[NW][TB];
+
+    const int t = threadIdx.x, l = t & 63, w = t >> 6;
+    const int hf = l / CPW;                       // which 64 rows of the column
+    const int col = w * CPW + (l % CPW);          // this lane's column
+    const size_t nh = blockIdx.x;                 // sequence * H + head
+    const int h = (int)(nh % p.H);
+    const size_t sq = nh / p.H;                   // sequence
+    // State of this (sequence, head) through a buffer descriptor: the lane's
+    // offset in a VGPR, the row offset as a scalar, so the 64 row accesses need
+    // no per-row 64-bit address registers.  Non-temporal: streamed once.
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.state + nh * (size_t)(DK * DV)), 0, (int)(DK * DV * sizeof(float)), 0x00020000);
+    const int lane_off = ((hf * RH) * DV + col) * (int)sizeof(float);
+    constexpr int ROW = DV * (int)sizeof(float), NT_AUX = 2;
+
+    float st[RH];
+#pragma unroll
+    for (int r = 0; r < RH; ++r)
+        st[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, lane_off, r * ROW, NT_AUX));
+
+    int n_rep = p.T_replay;
+    if (p.n_replay) n_rep = min(max(p.n_replay[sq], 0), p.T_replay);
+    const int n_tok = n_rep + p.T_new;
+    const int commit_at = n_rep + p.n_commit;     // tokens applied before the write-back (0: none)
+    const float eA = p.A_log ? __expf(p.A_log[h]) : 0.f;
+    auto row_of = [&](int it) {                   // (s, t, h) row of token `it` of replay-then-new
+        return it < n_rep ? (sq * (size_t)p.T_replay + it) * p.H + h
+                          : (sq * (size_t)p.T_new + (it - n_rep)) * p.H + h;
+    };
+    const int r0h = hf * RH;                      // first row of this lane
+
+    for (int base = 0; base < n_tok; base += TB) {
+        const int nb = min(TB, n_tok - base);
+        const int jc = commit_at - 1 - base;      // commit token inside this block, if 0 <= jc < nb
+        // ---- stage the block's inputs: all loads first (one latency per block),
+        // then the per-row products into LDS ----
+        {
+            constexpr int RPT = (DK + NT - 1) / NT;  // staged rows per thread
+            constexpr int CPT = (DV + NT - 1) / NT;  // staged value columns per thread
+            T gz[TB][RPT], kk[TB][RPT], qq[TB][RPT], vr[TB][CPT], bt[TB];
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                const int it = base + j;
+                const bool ok = j < nb, rep = it < n_rep;
+                const size_t row = ok ? row_of(it) : 0;
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    const int r = t + i * NT;
+                    const bool rk = ok && r < DK;
+                    gz[j][i] = rk ? ((const T *)(rep ? p.g_r : p.g))[row * DK + r] : from_f<T>(0.f);
+                    kk[j][i] = rk ? ((const T *)(rep ? p.k_r : p.k))[row * DK + r] : from_f<T>(0.f);
+                    qq[j][i] = (rk && !rep) ? ((const T *)p.q)[row * DK + r] : from_f<T>(0.f);
+                }
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) {
+                    const int cc = t + i * NT;
+                    vr[j][i] = (ok && cc < DV) ? ((const T *)(rep ? p.v_r : p.v))[row * DV + cc] : from_f<T>(0.f);
+                }
+                bt[j] = (ok && t == 0) ? ((const T *)(rep ? p.beta_r : p.beta))[row] : from_f<T>(0.f);
+            }
+            float pr[RPT];                        // running product of alpha for this thread's rows
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) pr[i] = 1.f;
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                if (j >= nb) break;
+                float kq = 0.f;
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    const int r = t + i * NT;
+                    if (r < DK) {
+                        float g = to_f<T>(gz[j][i]);
+                        g = p.A_log ? gate_from_logit(g, eA, p.g_min) : clamp_logdecay(g, p.g_min);
+                        const float kr = to_f<T>(kk[j][i]), qr = to_f<T>(qq[j][i]);
+                        pr[i] *= __expf(g);
+                        s_kd[j][r] = pr[i] * kr;
+                        s_qd[j][r] = pr[i] * qr;
+                        s_ki[j][r] = kr / pr[i];
+                        if (j == jc) s_pc[r] = pr[i];
+                        if (j == nb - 1) s_pe[r] = pr[i];
+                        kq += kr * qr;
+                    }
+                }
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
+                if (l == 0) s_kqw[w][j] = kq;
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) {
+                    const int cc = t + i * NT;
+                    if (cc < DV) s_v[j][cc] = to_f<T>(vr[j][i]);
+                }
+                if (t == 0) s_b[j] = to_f<T>(bt[j]);
+            }
+        }
+        __syncthreads();
+        // Rows in groups of GR; the scheduling barriers keep the compiler from
+        // hoisting every group's LDS reads (which would need ~3 x 64 registers).
+        constexpr int GR = 16;
+        for (int j = 0; j < nb; ++j) {
+            const int it = base + j;
+            const bool rep = it < n_rep;          // uniform across the workgroup
+            const float *kd = &s_kd[j][r0h], *qd = &s_qd[j][r0h], *ki = &s_ki[j][r0h];
+            float pp = 0.f, rr = 0.f;
+#pragma unroll
+            for (int g0 = 0; g0 < RH; g0 += GR) {
+#pragma unroll
+                for (int r = g0; r < g0 + GR; r += 4) {
+                    const f32x4 k4 = *reinterpret_cast<const f32x4 *>(kd + r);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pp += st[r + e] * k4[e];
+                }
+                if (!rep) {
+#pragma unroll
+                    for (int r = g0; r < g0 + GR; r += 4) {
+                        const f32x4 q4 = *reinterpret_cast<const f32x4 *>(qd + r);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) rr += st[r + e] * q4[e];
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (NH == 2) {                        // the other 64 rows of the column
+                pp += __shfl_xor(pp, 32);
+                if (!rep) rr += __shfl_xor(rr, 32);
+            }
+            const float d = s_b[j] * (s_v[j][col] - pp);
+            if (!rep && hf == 0) {
+                float kq = 0.f;
+#pragma unroll
+                for (int x = 0; x < NW; ++x) kq += s_kqw[x][j];
+                ((T *)p.o)[row_of(it) * DV + col] = from_f<T>(p.scale * (rr + d * kq));
+            }
+#pragma unroll
+            for (int g0 = 0; g0 < RH; g0 += GR) {
+#pragma unroll
+                for (int r = g0; r < g0 + GR; r += 4) {
+                    const f32x4 i4 = *reinterpret_cast<const f32x4 *>(ki + r);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) st[r + e] += i4[e] * d;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (j == jc) {                        // write back the true state X * P
+#pragma unroll
+                for (int r = 0; r < RH; r += 4) {
+                    const f32x4 p4 = *reinterpret_cast<const f32x4 *>(&s_pc[r0h + r]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, st[r + e] * p4[e]), srs,
+                                                              lane_off, (r + e) * ROW, NT_AUX);
+                }
+            }
+        }
+        if (base + TB < n_tok) {
+            // Leave the scaled frame before the next block restarts the products.
+#pragma unroll
+            for (int r = 0; r < RH; r += 4) {
+                const f32x4 p4 = *reinterpret_cast<const f32x4 *>(&s_pe[r0h + r]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[r + e] *= p4[e];
+            }
+            __syncthreads();  // the block is read to the end before the next is staged
+        }
+    }
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_replay_t(const ReplayParams &p, hipStream_t stream)
+{
+    const unsigned grid = (unsigned)((size_t)p.N * p.H);
+    const dim3 block(DV * (DK / 64));
+    if (p.T_replay + p.T_new == 1)  // one token per sequence: the single decode step
+        hipLaunchKernelGGL((replay_kernel<T, DK, DV, 1>), dim3(grid), block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((replay_kernel<T, DK, DV, 8>), dim3(grid), block, 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_recurrent_replay(int dtype_bf16, int Dk, int Dv, const ReplayParams &p, hipStream_t stream)
+{
+#define KDA_REPLAY_CASE(TT, DKV, DVV) \
+    if (Dk == DKV && Dv == DVV) return launch_replay_t<TT, DKV, DVV>(p, stream);
+    if (dtype_bf16) {
+        KDA_REPLAY_CASE(bf16, 64, 64)
+        KDA_REPLAY_CASE(bf16, 64, 128)
+        KDA_REPLAY_CASE(bf16, 128, 64)
+        KDA_REPLAY_CASE(bf16, 128, 128)
+    } else {
+        KDA_REPLAY_CASE(float, 64, 64)
+        KDA_REPLAY_CASE(float, 64, 128)
+        KDA_REPLAY_CASE(float, 128, 64)
+        KDA_REPLAY_CASE(float, 128, 128)
+    }
+#undef KDA_REPLAY_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -11,7 +11,9 @@
  * kda_chunk_fwd evaluates eq. (1) over whole sequences in the chunkwise-parallel
  * form of eqs. (3)-(4) (chunk size 64, 16-token sub-tiles); kda_recurrent_step
  * applies eq. (1) to one token per sequence with the state updated in place
- * (§5.4.2, "KDA" paragraph: the decode state is updated in place every step).
+ * (§5.4.2, "KDA" paragraph: the decode state is updated in place every step);
+ * kda_recurrent_replay runs a speculative-decoding window (replayed accepted
+ * tokens plus new tokens) in one pass over the in-place state (same paragraph).
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; all tensors are
@@ -147,6 +149,51 @@ typedef struct {
 } kda_step_args_t;
 
 KDA_API kda_status_t kda_recurrent_step(const kda_step_args_t *args, void *stream);
+
+/*
+ * Speculative-decoding step with replay ("Kimi K3 Technical Report", §5.4.2,
+ * "KDA" paragraph).  With multi-token drafts the in-place state cannot be
+ * rolled back once it has moved past a rejected draft, and keeping a state
+ * snapshot per draft position multiplies the state traffic.  The state after
+ * any accepted draft prefix is fixed by the drafts' projected inputs, which are
+ * much smaller, so the caller keeps those and this call rebuilds the accepted
+ * state on chip: for each sequence s and head h, in ONE pass over the state,
+ *   1. replay: the first n_replay[s] tokens of the cached window (k_r, v_r,
+ *      g_r, beta_r; their outputs were produced by an earlier call) go through
+ *      eq. (1) with no output;
+ *   2. new window: tokens 0 .. T_new-1 (q, k, v, g, beta) go through eq. (1)
+ *      and o[s, t] receives each token's output;
+ *   3. the state written back is the one after the replayed tokens and the
+ *      first n_commit tokens of the new window (typically 1: the bonus token
+ *      is certain, the drafts behind it are not); if that count is 0 the state
+ *      is left untouched.
+ * With T_replay = 0 and n_commit = T_new this is T_new decode steps in one
+ * pass; with n_commit = 0 it only verifies.
+ *   k_r, g_r : [N, T_replay, H, Dk]   v_r : [N, T_replay, H, Dv]   beta_r : [N, T_replay, H]
+ *   q, k, g  : [N, T_new, H, Dk]      v, o : [N, T_new, H, Dv]    beta : [N, T_new, H]
+ *   n_replay : [N] int32 on the device, or NULL (= T_replay for every sequence);
+ *              values are clamped to [0, T_replay] on the device
+ *   state    : [N, H, Dk, Dv] float32, in place
+ * Requirements: N >= 0, H >= 1, T_replay >= 0, T_new >= 0, 0 <= n_commit <=
+ * T_new; the replay tensors may be NULL when T_replay = 0 and the new-window
+ * tensors when T_new = 0.  Dk, Dv, dtype, A_log / g and alignment as for
+ * kda_recurrent_step; the state must not alias any other argument.
+ */
+typedef struct {
+    int32_t N, H, Dk, Dv;
+    int32_t dtype;                 /* kda_dtype_t */
+    int32_t T_replay, T_new, n_commit;
+    const void *k_r, *v_r, *g_r, *beta_r;
+    const int32_t *n_replay;
+    const void *q, *k, *v, *g, *beta;
+    const float *A_log;
+    float g_min;
+    float scale;
+    float *state;
+    void *o;
+} kda_replay_args_t;
+
+KDA_API kda_status_t kda_recurrent_replay(const kda_replay_args_t *args, void *stream);
 
 /* Static description of a status code. */
 KDA_API const char *kda_status_string(kda_status_t status);

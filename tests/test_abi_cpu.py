@@ -144,6 +144,58 @@ def test_recurrent_step_zero_sequences_is_a_noop(lib):
     assert lib.kda_recurrent_step(ctypes.byref(a), None) == 0
 
 
+def _replay_args(**over):
+    a = kda.ReplayArgs()
+    a.N, a.H, a.Dk, a.Dv, a.dtype = 4, 2, 128, 128, kda.KDA_BF16
+    a.T_replay, a.T_new, a.n_commit = 3, 4, 1
+    for f in ("k_r", "v_r", "g_r", "beta_r", "n_replay", "q", "k", "v", "g", "beta", "state", "o"):
+        setattr(a, f, 0x10000)
+    a.g_min, a.scale = -5.0, 1.0
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(Dk=96), 2, "head dims"),
+    (dict(state=None), 1, "state is NULL"),
+    (dict(state=0x10008), 1, "state is not 16-byte aligned"),
+    (dict(n_commit=5), 1, "n_commit"),
+    (dict(n_commit=-1), 1, "n_commit"),
+    (dict(T_new=-1), 1, "T_new >= 0"),
+    (dict(T_replay=-2), 1, "T_replay >= 0"),
+    (dict(q=None), 1, "q is NULL"),
+    (dict(o=None), 1, "o is NULL"),
+    (dict(k_r=None), 1, "k_r is NULL"),
+    (dict(beta_r=0x10001), 1, "beta_r is not aligned"),
+    (dict(n_replay=0x10002), 1, "n_replay is not 4-byte aligned"),
+    (dict(H=0), 1, "H >= 1"),
+    (dict(dtype=7), 1, "dtype"),
+])
+def test_recurrent_replay_rejects_before_launch(lib, over, status, msg):
+    a = _replay_args(**over)
+    assert lib.kda_recurrent_replay(ctypes.byref(a), None) == status
+    assert msg in lib.kda_last_error_message().decode()
+
+
+@pytest.mark.parametrize("over", [
+    dict(N=0),                                                    # no sequences
+    dict(T_replay=0, T_new=0, n_commit=0, k_r=None, q=None, o=None),  # empty window
+])
+def test_recurrent_replay_noops(lib, over):
+    a = _replay_args(**over)
+    assert lib.kda_recurrent_replay(ctypes.byref(a), None) == 0
+
+
+def test_recurrent_replay_window_pointers_only_when_used(lib):
+    """Replay tensors may be NULL with T_replay = 0, new-window tensors with T_new = 0
+    (checked on N = 0 so that nothing is launched)."""
+    a = _replay_args(N=0, T_replay=0, k_r=None, v_r=None, g_r=None, beta_r=None, n_replay=None)
+    assert lib.kda_recurrent_replay(ctypes.byref(a), None) == 0
+    a = _replay_args(N=0, T_new=0, n_commit=0, q=None, k=None, v=None, g=None, beta=None, o=None)
+    assert lib.kda_recurrent_replay(ctypes.byref(a), None) == 0
+
+
 def test_python_binding_requires_device_tensors(lib):
     x = torch.zeros(1, 8, 2, 64)
     with pytest.raises(ValueError, match="device tensor"):

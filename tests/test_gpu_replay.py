@@ -1,0 +1,213 @@
+"""GPU parity of the speculative-decoding step with replay ("Kimi K3 Technical
+Report", §5.4.2, "KDA" paragraph: accepted draft tokens are rebuilt on chip from
+their cached projected inputs, and the replayed tokens, the bonus token and the
+next draft window share one pass over the in-place state).
+
+Reference: the fp64 oracle runs, per sequence, the replayed tokens followed by
+the new window through eq. (1) token by token; the committed state is the
+oracle's final state over the replayed tokens plus the first n_commit new ones."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from kda_testutil import TOL, np64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_20_amd as kda
+    kda.load_library()
+
+
+def _workload(dtype=torch.bfloat16, Dk=128, Dv=128, seed=50, A_uniform=1.0):
+    return dataclasses.replace(W.WORKLOADS["decode_512_spec"], dtype=dtype, Dk=Dk, Dv=Dv, seed=seed,
+                               A_uniform=A_uniform)
+
+
+def _oracle(d, call, n_commit, heads=None, seqs=None, z_mode=True, scale=1.0):
+    """(o of the new window [N_sel, Tn, H_sel, Dv], committed state [N_sel, H_sel, Dk, Dv])."""
+    state = d["state"]
+    N = state.shape[0]
+    seqs = list(range(N)) if seqs is None else list(seqs)
+    hs = slice(None) if heads is None else list(heads)
+    Tr = 0 if call.get("k_r") is None else call["k_r"].shape[1]
+    Tn = 0 if call.get("q") is None else call["q"].shape[1]
+    nrep = [Tr] * N if call.get("n_replay") is None else [int(x) for x in call["n_replay"].cpu()]
+    nrep = [min(max(r, 0), Tr) for r in nrep]
+    sel = lambda t: None if t is None else np64(t)[:, :, hs]
+    kr, vr, zr, br = (sel(call.get(x)) for x in ("k_r", "v_r", "z_r", "beta_r"))
+    q, k, v, z, b = (sel(call.get(x)) for x in ("q", "k", "v", "z", "beta"))
+
+    def run(n_new):
+        parts = {x: [] for x in "qkvzb"}
+        lens = []
+        for s in seqs:
+            r = nrep[s]
+            if r:
+                parts["q"].append(np.zeros_like(kr[s, :r]))
+                for x, src in zip("kvzb", (kr, vr, zr, br)):
+                    parts[x].append(src[s, :r])
+            if n_new:
+                for x, src in zip("qkvzb", (q, k, v, z, b)):
+                    parts[x].append(src[s, :n_new])
+            lens.append(r + n_new)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        H = state.shape[1] if heads is None else len(heads)
+        Dk, Dv = state.shape[2], state.shape[3]
+        cat = lambda x, shp: np.concatenate(parts[x]) if parts[x] else np.zeros((0,) + shp)
+        A = np64(d["A_log"])[hs] if z_mode else None
+        o, hT = oracle.forward(cat("q", (H, Dk)), cat("k", (H, Dk)), cat("v", (H, Dv)), cat("z", (H, Dk)),
+                               cat("b", (H,)), cu_seqlens=cu, h0=np64(state)[seqs][:, hs], A_log=A,
+                               g_min=d["g_min"], scale=scale)
+        return o, hT, cu
+
+    o_all, _, cu = run(Tn)
+    o_new = np.stack([o_all[cu[i] + nrep[s]: cu[i + 1]] for i, s in enumerate(seqs)]) if Tn else None
+    _, h_commit, _ = run(n_commit)
+    return o_new, h_commit
+
+
+def _gpu_call(d, call, n_commit, z_mode=True, replay=True, scale=1.0):
+    import gated_delta_rule_20_amd as kda
+    rep = (call["k_r"], call["v_r"], call["z_r"], call["beta_r"]) if replay and call.get("k_r") is not None else None
+    has_new = call.get("q") is not None
+    o = kda.recurrent_replay(call.get("q") if has_new else None, call.get("k"), call.get("v"), call.get("z"),
+                             call.get("beta"), d["state"], replay=rep, n_replay=call.get("n_replay"),
+                             n_commit=n_commit, A_log=d["A_log"] if z_mode else None, g_min=d["g_min"],
+                             scale=scale)
+    torch.cuda.synchronize()
+    return o
+
+
+def _check(d, call, n_commit, z_mode=True, scale=1.0):
+    dt = call["k"].dtype if call.get("k") is not None else call["k_r"].dtype
+    ro, rh = _oracle(d, call, n_commit, z_mode=z_mode, scale=scale)
+    o = _gpu_call(d, call, n_commit, z_mode=z_mode, scale=scale)
+    e_s = rel_err(np64(d["state"]), rh)
+    e_o = rel_err(np64(o), ro) if o is not None else 0.0
+    print(f"rel err o={e_o:.3e} state={e_s:.3e}")
+    assert e_o <= TOL[dt] and e_s <= TOL[dt], (e_o, e_s)
+
+
+@pytest.mark.parametrize("n_commit", [0, 1, 4])
+def test_replay_bf16(n_commit):
+    """bf16, d = 128: a cached window of 4 with accepted counts 0..4 (every case
+    present; 4 is the whole window), 4 new tokens."""
+    d = W.make_spec_decode(_workload(seed=51), device="cuda", N=6, H=3, T_replay=4, calls=1)
+    call = d["calls"][0]
+    call["n_replay"] = torch.tensor([0, 1, 2, 3, 4, 2], dtype=torch.int32, device="cuda")
+    _check(d, call, n_commit)
+
+
+def test_replay_fp32():
+    d = W.make_spec_decode(_workload(torch.float32, 64, 64, seed=52), device="cuda", N=3, H=2,
+                           T_replay=3, T_new=5, calls=1, accept_range=(0, 3))
+    _check(d, d["calls"][0], 2)
+
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 128), (128, 64), (64, 64)])
+def test_replay_head_dims(Dk, Dv):
+    d = W.make_spec_decode(_workload(Dk=Dk, Dv=Dv, seed=53), device="cuda", N=4, H=2, calls=1)
+    _check(d, d["calls"][0], 1)
+
+
+def test_replay_logdecay_mode():
+    """g given directly (A_log = NULL), drawn as -5 * U(0, 1)."""
+    d = W.make_spec_decode(_workload(seed=54), device="cuda", N=4, H=2, calls=1)
+    call = d["calls"][0]
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    for key in ("z", "z_r"):
+        call[key] = (-5.0 * torch.rand(call[key].shape, generator=gen, device="cuda")).to(call[key].dtype)
+    _check(d, call, 1, z_mode=False)
+
+
+def test_replay_scale_and_all_replayed():
+    """n_replay = NULL replays the whole cached window; a non-unit query scale."""
+    d = W.make_spec_decode(_workload(seed=55), device="cuda", N=3, H=2, calls=1)
+    call = d["calls"][0]
+    call["n_replay"] = None
+    _check(d, call, 2, scale=0.125)
+
+
+def test_replay_only():
+    """No new window: the state advances over the accepted tokens and nothing is output."""
+    d = W.make_spec_decode(_workload(seed=56), device="cuda", N=4, H=2, calls=1)
+    call = d["calls"][0]
+    for key in ("q", "k", "v", "z", "beta"):
+        call[key] = None
+    _check(d, call, 0)
+
+
+def test_verify_only_leaves_state_untouched():
+    """Nothing accepted and nothing committed: outputs for the window, state bit-identical."""
+    d = W.make_spec_decode(_workload(seed=57), device="cuda", N=4, H=2, calls=1)
+    call = d["calls"][0]
+    call["n_replay"] = torch.zeros(4, dtype=torch.int32, device="cuda")
+    before = d["state"].clone()
+    ro, _ = _oracle(d, call, 0)
+    o = _gpu_call(d, call, 0)
+    assert torch.equal(d["state"], before)
+    assert rel_err(np64(o), ro) <= TOL[torch.bfloat16]
+
+
+def test_multi_token_equals_single_steps():
+    """No cached window and every token committed: the same as T single decode steps."""
+    import gated_delta_rule_20_amd as kda
+    d = W.make_spec_decode(_workload(seed=58), device="cuda", N=5, H=3, T_new=3, calls=1)
+    call = d["calls"][0]
+    s1 = d["state"].clone()
+    o = _gpu_call(d, call, 3, replay=False)
+    outs = []
+    for t in range(3):
+        outs.append(kda.recurrent_step(call["q"][:, t].contiguous(), call["k"][:, t].contiguous(),
+                                       call["v"][:, t].contiguous(), call["z"][:, t].contiguous(),
+                                       call["beta"][:, t].contiguous(), s1, A_log=d["A_log"], g_min=d["g_min"]))
+    torch.cuda.synchronize()
+    ref_o = torch.stack(outs, 1)
+    assert rel_err(np64(o), np64(ref_o)) <= 1e-6
+    assert rel_err(np64(d["state"]), np64(s1)) <= 1e-6
+
+
+def test_replay_full_size_sampled():
+    """decode_512_spec at full size (N = 512, H = 32, d = 128), one call; the oracle
+    checks 24 sampled (sequence, head) pairs."""
+    d = W.make_spec_decode(W.WORKLOADS["decode_512_spec"], device="cuda", calls=1)
+    call = d["calls"][0]
+    rng = np.random.default_rng(0)
+    seqs = sorted(rng.choice(512, 12, replace=False).tolist())
+    heads = [0, 31]
+    ro, rh = _oracle(d, call, 1, heads=heads, seqs=seqs)
+    o = _gpu_call(d, call, 1)
+    go = np64(o)[seqs][:, :, heads]
+    gs = np64(d["state"])[seqs][:, heads]
+    e_o, e_s = rel_err(go, ro), rel_err(gs, rh)
+    print(f"rel err o={e_o:.3e} state={e_s:.3e}")
+    assert e_o <= TOL[torch.bfloat16] and e_s <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("n_commit", [1, 7])
+def test_replay_long_window(n_commit):
+    """Windows longer than one staged block of 8 tokens (replay up to 6, 7 new):
+    the commit falls in the first or the second block."""
+    d = W.make_spec_decode(_workload(seed=59), device="cuda", N=5, H=2, T_replay=6, T_new=7, calls=1)
+    call = d["calls"][0]
+    call["n_replay"] = torch.tensor([6, 0, 3, 6, 1], dtype=torch.int32, device="cuda")
+    _check(d, call, n_commit)
+
+
+def test_replay_strong_decay():
+    """Hard-forgetting gates (g = g_min) over a long window: the per-block decay
+    products reach exp(-40), the range the kernel's scaled frame must hold."""
+    d = W.make_spec_decode(_workload(seed=60), device="cuda", N=3, H=2, T_replay=4, T_new=8, calls=1)
+    call = d["calls"][0]
+    for key in ("z", "z_r"):
+        call[key] = torch.full_like(call[key], W.Z_SATURATE)
+    _check(d, call, 8)

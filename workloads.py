@@ -19,6 +19,12 @@ Open Frontier Intelligence" §2.1.1 notation, d_k = d_v = d):
                      530,033), H=32, d=128, per-sequence initial states.
 * ``decode_512``     512 sequences x 1 token per step, H=32, d=128, 64 steps
                      with fresh inputs, fp32 state [512, 32, 128, 128].
+* ``decode_512_spec`` speculative decoding on the decode_512 shapes, 3 drafts
+                     per step: per call, the cached window holds the previous
+                     step's 3 drafts, of which 0..3 (uniform per sequence) were
+                     accepted and are replayed; the new window holds 4 tokens
+                     (the bonus token, which is certain and committed, and 3 new
+                     drafts).  16 calls with fresh inputs.
 
 Common distributions: q, k ~ N(0, 1) then L2-normalised over d_k per (token,
 head) in fp32 (eq. (2) applies L2Norm before the core); v ~ N(0, 1);
@@ -72,6 +78,8 @@ WORKLOADS = {
                           n_seqs=64, len_range=(128, 16384), len_seed=247, A_uniform=1.0),
     "decode_512": Workload("decode_512", torch.bfloat16, H=32, Dk=128, Dv=128, seed=4,
                            B=512, T=1, decode_steps=64),
+    "decode_512_spec": Workload("decode_512_spec", torch.bfloat16, H=32, Dk=128, Dv=128, seed=5,
+                                B=512, T=4, len_range=(0, 3), decode_steps=16),
 }
 
 # Decay logit that saturates the gate's sigmoid (hard forgetting, g = g_min),
@@ -195,3 +203,45 @@ def make_decode(w: Workload, device="cpu", N: int | None = None, H: int | None =
 def n_tokens(inp) -> int:
     q = inp["q"]
     return int(math.prod(q.shape[:-2]))
+
+
+
+def make_spec_decode(w: Workload, device="cpu", N: int | None = None, H: int | None = None,
+                     T_replay: int | None = None, T_new: int | None = None, calls: int | None = None,
+                     accept_range=None):
+    """State and per-call inputs of a speculative-decoding workload.  Returns
+    dict with ``state`` [N, H, Dk, Dv] fp32 and ``calls``: a list of dicts,
+    each with the cached window (k_r, z_r [N, Tr, H, Dk], v_r [N, Tr, H, Dv],
+    beta_r [N, Tr, H]; Tr defaults to the workload's window minus the bonus
+    token), ``n_replay`` [N] int32 (accepted drafts, drawn on the CPU from
+    ``accept_range``, inclusive) and the new window (q, k, z, v, beta shaped
+    like the cached window with T_new tokens)."""
+    N = N or w.B
+    H = H or w.H
+    T_new = w.T if T_new is None else T_new
+    T_replay = w.T - 1 if T_replay is None else T_replay
+    calls = calls or w.decode_steps
+    lo, hi = accept_range or w.len_range
+    gen = _gen(w.seed, device)
+    cpu = _gen(w.seed + 7, "cpu")
+    state = _normal((N, H, w.Dk, w.Dv), gen, device) * w.h0_std
+    A = (torch.rand((H,), generator=gen, device=device) * 2 - 1) * w.A_uniform if w.A_uniform > 0 \
+        else torch.zeros((H,), device=device)
+    dt = w.dtype
+
+    def window(T):
+        q = _unit_rows(_normal((N, T, H, w.Dk), gen, device))
+        k = _unit_rows(_normal((N, T, H, w.Dk), gen, device))
+        v = _normal((N, T, H, w.Dv), gen, device)
+        beta = torch.sigmoid(_normal((N, T, H), gen, device))
+        z = _normal((N, T, H, w.Dk), gen, device)
+        return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), z=z.to(dt), beta=beta.to(dt))
+
+    out = []
+    for _ in range(calls):
+        old, new = window(T_replay), window(T_new)
+        n_rep = torch.randint(lo, hi + 1, (N,), generator=cpu, dtype=torch.int32)
+        out.append(dict(k_r=old["k"], v_r=old["v"], z_r=old["z"], beta_r=old["beta"],
+                        n_replay=n_rep.to(device), q=new["q"], k=new["k"], v=new["v"], z=new["z"],
+                        beta=new["beta"]))
+    return dict(state=state, A_log=A.float(), calls=out, g_min=G_MIN)
