@@ -253,6 +253,18 @@ __device__ __forceinline__ int ld_uniform(const int32_t *ptr, int i)
     return ((const __attribute__((address_space(4))) int32_t *)ptr)[i];
 }
 
+// Raw buffer load of a 2-, 4- or 8-byte vector; offsets at or past the
+// descriptor's record count read as zero.
+template <typename V> __device__ __forceinline__ V buf_load(__amdgpu_buffer_rsrc_t rs, int voff)
+{
+    if constexpr (sizeof(V) == 2)
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b16(rs, voff, 0, 0));
+    else if constexpr (sizeof(V) == 4)
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, 0));
+    else
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, 0));
+}
+
 // Token range of chunk c; false if c is past the last chunk (packed tail).
 __device__ __forceinline__ bool locate_chunk(const PrefillParams &p, int c, int &tok0, int &len)
 {
@@ -288,7 +300,9 @@ __device__ __forceinline__ bool next_item(const PrefillParams &p, int &i, int &c
     return false;
 }
 
-template <typename T, int DK, int DV>
+// ZM: decay logits z with the eq. (5) gate (A_log given), else log-decays g;
+// a template parameter so the elementwise pass carries no per-element branch.
+template <typename T, int DK, int DV, bool ZM>
 __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 {
     using BL = Block<T, DK, DV>;
@@ -301,7 +315,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
     extern __shared__ __align__(16) char smem_raw[];
     SM &sm = *reinterpret_cast<SM *>(smem_raw);
 
-    const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, x = l & 15;
+    const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 4, x = l & 15;
     const int ch0 = CPT * l;  // first channel of this lane in the elementwise phase
     const int m0 = w & 3, hf = w >> 2, tb = seg_base(w);  // elementwise: tile, half, first token
 
@@ -324,14 +338,20 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         // its last use below, so the loads issue between this item's VALU work.
         int i2 = i + gridDim.x, c2 = 0, h2 = 0, tok2 = 0, len2 = 0;
         const bool have2 = next_item(p, i2, c2, h2, tok2, len2);
-        const T *ng = (const T *)p.g, *nk = (const T *)p.k, *nq = (const T *)p.q, *nv = (const T *)p.v;
-        auto nrow = [&](int r, bool &ok) {
-            ok = have2 && tb + r < len2;
-            return (size_t)(tok2 + tb + r) * p.H + h2;
-        };
-        ku zk;
-#pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) zk[cc] = from_f<T>(0.f);
+        // The next item's rows of this wave through buffer descriptors: base at its
+        // first token (uniform), lane offset plus token offset in one VGPR shared by
+        // g, k and q, and a record count that ends at the last valid token, so tokens
+        // past the chunk read as zero without a mask.
+        const int nvalid = have2 ? min(max(len2 - tb, 0), HT) : 0;
+        const size_t row0 = ((size_t)(tok2 + tb) * p.H + h2);
+        const int rowk = p.H * DK * (int)sizeof(T), rowv = p.H * DV * (int)sizeof(T);
+        const int reck = nvalid ? (nvalid - 1) * rowk + DK * (int)sizeof(T) : 0;
+        const int recv = nvalid ? (nvalid - 1) * rowv + DV * (int)sizeof(T) : 0;
+        const __amdgpu_buffer_rsrc_t rsg = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.g + row0 * DK), 0, reck, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.k + row0 * DK), 0, reck, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsq = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.q + row0 * DK), 0, reck, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.v + row0 * DV), 0, recv, 0x00020000);
+        const int offk = ch0 * (int)sizeof(T), offv = CPV * l * (int)sizeof(T);
         float lam2[HT][CPT];  // (lam_r - B_m) log2(e) for this wave's tokens (tile m = w % 4)
         {
             const float cz = -__expf(raw.alog) * LOG2E;  // exp(-e^A z) = exp2(cz z)
@@ -344,7 +364,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) {
                     const float z = to_f<T>(raw.g[r][cc]);
-                    float g2 = p.A_log ? gm2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(cz * z))
+                    float g2 = ZM ? gm2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(cz * z))
                                        : clamp_logdecay(z, p.g_min) * LOG2E;
                     g2 = (tb + r < len) ? g2 : 0.f;  // tokens past the end keep S unchanged
                     run[cc] += g2;
@@ -358,7 +378,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         {
             const int bt = tb + l;
             raw.beta = (have2 && l < HT && bt < len2) ? ((const T *)p.beta)[(size_t)(tok2 + bt) * p.H + h2] : from_f<T>(0.f);
-            raw.alog = (have2 && p.A_log) ? p.A_log[h2] : 0.f;
+            raw.alog = (have2 && ZM) ? p.A_log[h2] : 0.f;
         }
         lds_barrier();
         {
@@ -416,13 +436,9 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     *reinterpret_cast<ku *>(&sm.y.KC[128 + r][ch0]) = kx2_;
                 }
                 if (m0 == 1) *reinterpret_cast<ku *>(&sm.y.KC[144 + r][ch0]) = kx1_;
-                {
-                    bool ok;
-                    const size_t row = nrow(r0, ok);
-                    raw.g[r0] = ok ? *reinterpret_cast<const ku *>(ng + row * DK + ch0) : zk;
-                    raw.k[r0] = ok ? *reinterpret_cast<const ku *>(nk + row * DK + ch0) : zk;
-                    raw.q[r0] = ok ? *reinterpret_cast<const ku *>(nq + row * DK + ch0) : zk;
-                }
+                raw.g[r0] = buf_load<ku>(rsg, offk + r0 * rowk);
+                raw.k[r0] = buf_load<ku>(rsk, offk + r0 * rowk);
+                raw.q[r0] = buf_load<ku>(rsq, offk + r0 * rowk);
             }
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) {
@@ -441,15 +457,8 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 for (int r = 0; r < HT; ++r) col[r] = raw.v[r][cv];
                 *reinterpret_cast<tok8 *>(&sm.VT[CPV * l + cv][tb]) = col;
             }
-            typename R::vu zv;
 #pragma unroll
-            for (int cv = 0; cv < CPV; ++cv) zv[cv] = from_f<T>(0.f);
-#pragma unroll
-            for (int r = 0; r < HT; ++r) {
-                bool ok;
-                const size_t row = nrow(r, ok);
-                raw.v[r] = ok ? *reinterpret_cast<const typename R::vu *>(nv + row * DV + CPV * l) : zv;
-            }
+            for (int r = 0; r < HT; ++r) raw.v[r] = buf_load<typename R::vu>(rsv, offv + r * rowv);
         }
         lds_barrier();
 
@@ -909,12 +918,18 @@ static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
     if (p.n_chunks_cap > 0) {
         const size_t smem = sizeof(IntraSmem<T, DK, DV>);
         static_assert(sizeof(IntraSmem<T, DK, DV>) <= 160 * 1024, "intra-chunk LDS exceeds 160 KiB");
-        static const hipError_t attr = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV>,
-                                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (attr != hipSuccess) return attr;
+        static const hipError_t attr_z = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, true>,
+                                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        static const hipError_t attr_g = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, false>,
+                                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (attr_z != hipSuccess) return attr_z;
+        if (attr_g != hipSuccess) return attr_g;
         const long items = (long)p.n_chunks_cap * p.H;
         const unsigned grid = (unsigned)(items < intra_grid() ? items : intra_grid());
-        hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV>), dim3(grid), dim3(64 * IWAVES), smem, st, p);
+        if (p.A_log)
+            hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, true>), dim3(grid), dim3(64 * IWAVES), smem, st, p);
+        else
+            hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, false>), dim3(grid), dim3(64 * IWAVES), smem, st, p);
     }
     const long npairs = (long)p.N * p.H;
     const unsigned grid = (unsigned)(((npairs + 7) / 8) * 8 * (DV / 16));
