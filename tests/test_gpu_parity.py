@@ -76,6 +76,18 @@ def test_logdecay_mode():
     _check(inp, z_mode=False)
 
 
+@pytest.mark.parametrize("dt", ["prefill_8k", "tiny_fp32"])
+def test_weak_decay_long_memory(dt):
+    """Log-decays g ~ -U(0, 0.002) and beta / 10: the state carries information over
+    hundreds of tokens, so every chunk-to-chunk hand-off of the chain shows in the
+    output (with the workloads' own gates the state forgets within ~10 tokens)."""
+    inp = _small(dt, T=1000, H=3, seed=13)
+    gen = torch.Generator(device="cuda").manual_seed(6)
+    inp["z"] = (-0.002 * torch.rand(inp["z"].shape, generator=gen, device="cuda")).to(inp["q"].dtype)
+    inp["beta"] = (inp["beta"].float() * 0.1).to(inp["q"].dtype)
+    _check(inp, z_mode=False)
+
+
 def test_forced_channels_short():
     """Hard-forgetting (g = -5) and near-unit (g ~ -1e-3) channels stress the
     range of the cumulative decay."""
