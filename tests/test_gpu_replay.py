@@ -211,3 +211,18 @@ def test_replay_strong_decay():
     for key in ("z", "z_r"):
         call[key] = torch.full_like(call[key], W.Z_SATURATE)
     _check(d, call, 8)
+
+
+def test_replay_weak_decay():
+    """Log-decays g ~ -U(0, 0.002) and beta / 10: the entering state still dominates
+    after the window, so the committed state checks every row and column of the
+    state's read-modify-write (with the workloads' gates it fades within the window)."""
+    d = W.make_spec_decode(_workload(seed=61), device="cuda", N=4, H=2, T_replay=4, T_new=4, calls=1)
+    d["state"] = torch.randn_like(d["state"])  # O(1) entering state
+    call = d["calls"][0]
+    gen = torch.Generator(device="cuda").manual_seed(10)
+    for key in ("z", "z_r"):
+        call[key] = (-0.002 * torch.rand(call[key].shape, generator=gen, device="cuda")).to(call[key].dtype)
+    for key in ("beta", "beta_r"):
+        call[key] = (call[key].float() * 0.1).to(call[key].dtype)
+    _check(d, call, 1, z_mode=False)
