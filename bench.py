@@ -157,6 +157,36 @@ def bench_decode(warmup_rounds=1):
                 N=N, H=H, bytes=nbytes, flops=flops)
 
 
+def bench_prefill_config(name, steps=5, warmup=2):
+    """One kda_chunk_fwd call over a whole prefill workload (fixed-length or packed)."""
+    w = W.WORKLOADS[name]
+    inp = W.make_prefill(w, device="cuda")
+    cu = inp["cu_seqlens"]
+    N = cu.numel() - 1 if cu is not None else inp["q"].shape[0]
+    o = torch.empty_like(inp["v"])
+    hT = torch.empty_like(inp["h0"])
+    nws = kda.chunk_fwd_workspace_size(inp["q"], inp["v"], cu_seqlens=cu, N=N if cu is not None else None)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["z"], inp["beta"], A_log=inp["A_log"], g_min=inp["g_min"],
+                      cu_seqlens=cu, initial_state=inp["h0"], out=o, final_state=hT, workspace=ws, stream=stream)
+
+    for i in range(warmup):
+        call(i)
+    per_call, _ = time_calls(call, steps, stream)
+    tokens = W.n_tokens(inp)
+    H, Dk = inp["q"].shape[-2:]
+    Dv = inp["v"].shape[-1]
+    nbytes, flops = prefill_counts(tokens, H, Dk, Dv, N)
+    ms = sum(per_call) / len(per_call)
+    del inp, o, hT, ws
+    return {"ms_per_call": ms, "ms_min": min(per_call), "tokens": tokens, "sequences": N,
+            "tokens_per_s": tokens / (ms / 1e3), "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+
+
 def spec_counts(N, H, Dk, Dv, n_replayed, T_new, elem=2):
     """Algorithmic bytes of one replay call: the state read and written once, the
     replayed tokens' k, g, v, beta, and the new window's q, k, g, v, beta and o."""
@@ -269,6 +299,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured GEMM / copy reference peaks")
     ap.add_argument("--no-spec", action="store_true", help="skip the speculative-decoding replay measurement")
+    ap.add_argument("--no-other", action="store_true", help="skip the prefill_128k and varlen_64 measurements")
     ap.add_argument("--mode", choices=["all", "prefill", "decode", "spec", "copy"], default="all",
                     help="prefill/decode/copy run one part only (for profiler runs); the JSON line "
                          "of the benchmark contract is printed in mode 'all'")
@@ -365,6 +396,12 @@ def main():
                          "algorithmic_bytes": sp["bytes"]},
             "us_per_call_by_new_window": window,
         }
+    if not args.no_other:
+        result["other_prefill"] = {
+            "prefill_128k: B=1 T=131072 H=32 d=128, 5% of decay channels forced each way": bench_prefill_config("prefill_128k"),
+            "varlen_64: 64 packed sequences, lengths U{128..16384}, 530,033 tokens, H=32 d=128": bench_prefill_config("varlen_64"),
+        }
+        torch.cuda.empty_cache()
     if not args.no_peaks:
         pk = measured_peaks()
         result["measured_peaks"] = pk
