@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = ["chunk_fwd", "recurrent_step", "recurrent_replay", "chunk_fwd_workspace_size", "load_library",
-           "KDAError", "LIB_PATH", "EXPORTED_SYMBOLS"]
+           "Fusion", "KDAError", "LIB_PATH", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 EXPORTED_SYMBOLS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_recurrent_step",
@@ -35,6 +35,13 @@ class KDAError(RuntimeError):
         self.status = status
 
 
+class LayerFusion(ctypes.Structure):
+    _fields_ = [("conv_width", ctypes.c_int32), ("conv_weight", ctypes.c_void_p),
+                ("conv_state", ctypes.c_void_p), ("conv_state_out", ctypes.c_void_p),
+                ("conv_checkpoints", ctypes.c_void_p), ("qk_norm_eps", ctypes.c_float),
+                ("gate", ctypes.c_void_p), ("o_norm_weight", ctypes.c_void_p), ("o_norm_eps", ctypes.c_float)]
+
+
 class ChunkFwdArgs(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
@@ -45,7 +52,8 @@ class ChunkFwdArgs(ctypes.Structure):
                 ("initial_state", ctypes.c_void_p), ("o", ctypes.c_void_p),
                 ("final_state", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("checkpoints", ctypes.c_void_p),
-                ("checkpoint_every", ctypes.c_int32), ("checkpoint_slots", ctypes.c_int32)]
+                ("checkpoint_every", ctypes.c_int32), ("checkpoint_slots", ctypes.c_int32),
+                ("fusion", ctypes.POINTER(LayerFusion))]
 
 
 class StepArgs(ctypes.Structure):
@@ -54,7 +62,8 @@ class StepArgs(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
                 ("g_min", ctypes.c_float), ("scale", ctypes.c_float),
-                ("state", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+                ("state", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("fusion", ctypes.POINTER(LayerFusion))]
 
 
 class ReplayArgs(ctypes.Structure):
@@ -66,7 +75,71 @@ class ReplayArgs(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
                 ("g_min", ctypes.c_float), ("scale", ctypes.c_float),
-                ("state", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+                ("state", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("q_r", ctypes.c_void_p), ("fusion", ctypes.POINTER(LayerFusion))]
+
+
+class Fusion:
+    """The layer's prologue (eq. (2)) and epilogue (eq. (6)) fused into a call.
+
+    Prologue (on when ``conv_weight`` is given, [H, 2*Dk + Dv, W] fp32, W <= 4):
+    q, k, v are the projections before the short convolution and beta holds
+    logits; the kernels apply ShortConv, Swish, L2Norm (q, k; eps ``qk_eps``)
+    and Sigmoid (beta).  ``conv_state`` [N, H, W-1, 2*Dk + Dv] in the input
+    dtype: read by chunk_fwd (None = zeros), updated in place by the decode
+    calls.  chunk_fwd also takes ``conv_state_out`` and, with checkpoints,
+    ``conv_checkpoints`` [N, slots, H, W-1, 2*Dk + Dv].
+    Epilogue (on when ``gate`` is given, logits shaped like the output):
+    the output becomes Sigmoid(gate) * RMSNorm(o~) with per-head weights
+    ``o_norm_weight`` [H, Dv] fp32 and eps ``o_eps``.
+    """
+
+    def __init__(self, conv_weight=None, conv_state=None, conv_state_out=None, conv_checkpoints=None,
+                 qk_eps: float = 1e-6, gate=None, o_norm_weight=None, o_eps: float = 1e-6):
+        self.conv_weight, self.conv_state = conv_weight, conv_state
+        self.conv_state_out, self.conv_checkpoints = conv_state_out, conv_checkpoints
+        self.qk_eps, self.gate, self.o_norm_weight, self.o_eps = qk_eps, gate, o_norm_weight, o_eps
+
+    def _args(self, N, H, Dk, Dv, dtype, out_shape, slots=None):
+        """Checked ctypes view; shapes are verified here since the ABI takes bare pointers."""
+        f = LayerFusion()
+        C = 2 * Dk + Dv
+        if self.conv_weight is not None:
+            w = _dev(self.conv_weight, "conv_weight", torch.float32)
+            if w.dim() != 3 or tuple(w.shape[:2]) != (H, C) or not 1 <= w.shape[2] <= 4:
+                raise ValueError(f"conv_weight must be [H, 2*Dk + Dv, W] = [{H}, {C}, 1..4], got {tuple(w.shape)}")
+            W = w.shape[2]
+            for name, t, lead in (("conv_state", self.conv_state, (N, H)),
+                                  ("conv_state_out", self.conv_state_out, (N, H)),
+                                  ("conv_checkpoints", self.conv_checkpoints, None)):
+                if t is None:
+                    continue
+                _dev(t, name, dtype)
+                want = (N, H, W - 1, C) if lead else (N, slots, H, W - 1, C)
+                if slots is None and lead is None:
+                    raise ValueError("conv_checkpoints needs checkpoints")
+                if tuple(t.shape) != want:
+                    raise ValueError(f"{name} must be {want}, got {tuple(t.shape)}")
+            f.conv_width = W
+            f.conv_weight = _ptr(w)
+            f.conv_state, f.conv_state_out = _ptr(self.conv_state), _ptr(self.conv_state_out)
+            f.conv_checkpoints = _ptr(self.conv_checkpoints)
+            f.qk_norm_eps = float(self.qk_eps)
+        elif any(t is not None for t in (self.conv_state, self.conv_state_out, self.conv_checkpoints)):
+            raise ValueError("convolution buffers given without conv_weight")
+        if self.gate is not None:
+            _dev(self.gate, "gate", dtype)
+            if tuple(self.gate.shape) != tuple(out_shape):
+                raise ValueError(f"gate must have the output's shape {tuple(out_shape)}, got {tuple(self.gate.shape)}")
+            wo = _dev(self.o_norm_weight, "o_norm_weight", torch.float32)
+            if wo is None or tuple(wo.shape) != (H, Dv):
+                raise ValueError(f"o_norm_weight must be [H, Dv] = {(H, Dv)}")
+            f.gate, f.o_norm_weight, f.o_norm_eps = _ptr(self.gate), _ptr(wo), float(self.o_eps)
+        return f
+
+    @property
+    def prologue(self) -> bool:
+        return self.conv_weight is not None
 
 
 _lib = None
@@ -175,7 +248,7 @@ def chunk_fwd_workspace_size(q, v, *, cu_seqlens=None, N=None) -> int:
 def chunk_fwd(q, k, v, g, beta, *, A_log=None, g_min: float = -5.0, scale: float = 1.0,
               cu_seqlens=None, initial_state=None, output_final_state: bool = True,
               out=None, final_state=None, workspace=None, stream=None,
-              checkpoints=None, checkpoint_every: int = 0):
+              checkpoints=None, checkpoint_every: int = 0, fusion: Fusion | None = None):
     """Chunkwise-parallel KDA forward.
 
     q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H] (bf16 or fp32).
@@ -187,6 +260,7 @@ def chunk_fwd(q, k, v, g, beta, *, A_log=None, g_min: float = -5.0, scale: float
     checkpoints: optional [N, slots, H, Dk, Dv] fp32; slot j receives the state
     after (j + 1) * checkpoint_every * 64 tokens of each sequence when that
     position lies strictly inside it (other slots are left as they are).
+    fusion: optional :class:`Fusion` (layer prologue / epilogue in the kernels).
     Returns (o, final_state or None).
     """
     lib = load_library()
@@ -230,14 +304,19 @@ def chunk_fwd(q, k, v, g, beta, *, A_log=None, g_min: float = -5.0, scale: float
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a = _chunk_args(q, k, v, g, beta, A_log, g_min, scale, cu_seqlens, N, initial_state,
                     out, final_state, workspace, ws_bytes, checkpoints, checkpoint_every)
+    if fusion is not None:
+        fa = fusion._args(N, H, Dk, Dv, q.dtype, out.shape,
+                          slots=None if checkpoints is None else checkpoints.shape[1])
+        a.fusion = ctypes.pointer(fa)
     _check(lib, "kda_chunk_fwd", lib.kda_chunk_fwd(ctypes.byref(a), _stream(stream, q.device)))
     return out, final_state
 
 
 def recurrent_step(q, k, v, g, beta, state, *, A_log=None, g_min: float = -5.0,
-                   scale: float = 1.0, out=None, stream=None):
+                   scale: float = 1.0, out=None, stream=None, fusion: Fusion | None = None):
     """One decode token per sequence, state [N, H, Dk, Dv] fp32 updated in
-    place.  q, k, g: [N, H, Dk]; v: [N, H, Dv]; beta: [N, H].  Returns o."""
+    place.  q, k, g: [N, H, Dk]; v: [N, H, Dv]; beta: [N, H].  ``fusion``: optional
+    :class:`Fusion` (its conv_state is updated in place too).  Returns o."""
     lib = load_library()
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -263,12 +342,16 @@ def recurrent_step(q, k, v, g, beta, state, *, A_log=None, g_min: float = -5.0,
     a.A_log = _ptr(A_log)
     a.g_min, a.scale = float(g_min), float(scale)
     a.state, a.o = _ptr(state), _ptr(out)
+    if fusion is not None:
+        fa = fusion._args(N, H, Dk, Dv, q.dtype, out.shape)
+        a.fusion = ctypes.pointer(fa)
     _check(lib, "kda_recurrent_step", lib.kda_recurrent_step(ctypes.byref(a), _stream(stream, q.device)))
     return out
 
 
 def recurrent_replay(q, k, v, g, beta, state, *, replay=None, n_replay=None, n_commit=None,
-                     A_log=None, g_min: float = -5.0, scale: float = 1.0, out=None, stream=None):
+                     A_log=None, g_min: float = -5.0, scale: float = 1.0, out=None, stream=None,
+                     q_r=None, fusion: Fusion | None = None):
     """Speculative-decoding step with replay, state [N, H, Dk, Dv] fp32 in place.
 
     New window: q, k, g [N, T, H, Dk]; v [N, T, H, Dv]; beta [N, T, H] (T may be 0
@@ -276,7 +359,9 @@ def recurrent_replay(q, k, v, g, beta, state, *, replay=None, n_replay=None, n_c
     of shapes [N, Tr, H, ...]; ``n_replay`` ([N] int32 on the device, or None = Tr)
     tokens of it are replayed first, without output.  The state written back is
     the one after the replayed tokens and the first ``n_commit`` new tokens
-    (default: all of them).  Returns o [N, T, H, Dv] (None when T = 0)."""
+    (default: all of them).  ``fusion``: optional :class:`Fusion`; with its
+    prologue the replayed window's query projections ``q_r`` [N, Tr, H, Dk] are
+    needed too.  Returns o [N, T, H, Dv] (None when T = 0)."""
     lib = load_library()
     ref = q if q is not None else replay[0]
     if ref.dtype not in _DTYPES:
@@ -326,5 +411,14 @@ def recurrent_replay(q, k, v, g, beta, state, *, replay=None, n_replay=None, n_c
     a.A_log = _ptr(A_log)
     a.g_min, a.scale = float(g_min), float(scale)
     a.state = _ptr(state)
+    if q_r is not None:
+        _dev(q_r, "q_r", dt)
+        if replay is None or q_r.shape != replay[0].shape:
+            raise ValueError("q_r must have k_r's shape")
+        a.q_r = _ptr(q_r)
+    if fusion is not None:
+        out_shape = out.shape if out is not None else (N, 0, H, Dv)
+        fa = fusion._args(N, H, Dk, Dv, dt, out_shape)
+        a.fusion = ctypes.pointer(fa)
     _check(lib, "kda_recurrent_replay", lib.kda_recurrent_replay(ctypes.byref(a), _stream(stream, state.device)))
     return out

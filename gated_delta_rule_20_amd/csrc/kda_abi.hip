@@ -34,6 +34,65 @@ kda_status_t check_common(int dtype, int Dk, int Dv, const float *A_log, float g
     return KDA_SUCCESS;
 }
 
+bool overlap(const void *a, const void *b, size_t bytes)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + bytes && y < x + bytes;
+}
+
+// Validates a kda_layer_fusion_t and fills the kernels' view of it.
+// prefill: kda_chunk_fwd (read-only conv_state, optional conv_state_out and
+// conv_checkpoints) vs the decode entry points (conv_state in place).
+kda_status_t check_fusion(const kda_layer_fusion_t *f, bool prefill, bool has_ckpt, int dtype, int N, int H,
+                          int Dk, int Dv, kda::FusionParams *out)
+{
+    *out = kda::FusionParams{};
+    if (!f) return KDA_SUCCESS;
+    if (f->conv_width < 0 || f->conv_width > 4)
+        return fail(KDA_ERROR_NOT_SUPPORTED, "conv_width=%d: must be 0 (no prologue) or 1..4", f->conv_width);
+    const size_t el = dtype == KDA_BF16 ? 2 : 4;
+    if (f->conv_width > 0) {
+        if (!f->conv_weight) return fail(KDA_ERROR_INVALID_VALUE, "conv_weight is NULL");
+        if (!aligned16(f->conv_weight)) return fail(KDA_ERROR_INVALID_VALUE, "conv_weight is not 16-byte aligned");
+        if (!(f->qk_norm_eps >= 0.0f)) return fail(KDA_ERROR_INVALID_VALUE, "qk_norm_eps must be >= 0");
+        const size_t cs_bytes = (size_t)N * H * (f->conv_width - 1) * (2 * Dk + Dv) * el;
+        const void *bufs[] = {f->conv_state, f->conv_state_out, f->conv_checkpoints};
+        const char *nm[] = {"conv_state", "conv_state_out", "conv_checkpoints"};
+        for (int i = 0; i < 3; ++i)
+            if (bufs[i] && !aligned16(bufs[i])) return fail(KDA_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", nm[i]);
+        if (prefill) {
+            if (f->conv_state && f->conv_state_out && cs_bytes > 0 && overlap(f->conv_state, f->conv_state_out, cs_bytes))
+                return fail(KDA_ERROR_INVALID_VALUE, "conv_state_out overlaps conv_state");
+            if (f->conv_checkpoints && !has_ckpt)
+                return fail(KDA_ERROR_INVALID_VALUE, "conv_checkpoints needs checkpoints");
+        } else {
+            if (f->conv_state_out || f->conv_checkpoints)
+                return fail(KDA_ERROR_INVALID_VALUE, "conv_state_out / conv_checkpoints are for kda_chunk_fwd only "
+                            "(decode updates conv_state in place)");
+            if (f->conv_width > 1 && !f->conv_state && N > 0)
+                return fail(KDA_ERROR_INVALID_VALUE, "conv_state is NULL (decode carries the convolution state)");
+        }
+    } else if (f->conv_weight || f->conv_state || f->conv_state_out || f->conv_checkpoints) {
+        return fail(KDA_ERROR_INVALID_VALUE, "convolution buffers given with conv_width = 0");
+    }
+    if (f->gate) {
+        if (!aligned16(f->gate)) return fail(KDA_ERROR_INVALID_VALUE, "gate is not 16-byte aligned");
+        if (!f->o_norm_weight) return fail(KDA_ERROR_INVALID_VALUE, "o_norm_weight is NULL");
+        if (!aligned16(f->o_norm_weight)) return fail(KDA_ERROR_INVALID_VALUE, "o_norm_weight is not 16-byte aligned");
+        if (!(f->o_norm_eps >= 0.0f)) return fail(KDA_ERROR_INVALID_VALUE, "o_norm_eps must be >= 0");
+    }
+    out->conv_w = f->conv_width;
+    out->conv_weight = f->conv_weight;
+    out->conv_state = f->conv_width > 1 ? f->conv_state : nullptr;
+    out->conv_state_out = f->conv_width > 1 ? f->conv_state_out : nullptr;
+    out->conv_ckpt = f->conv_width > 1 ? f->conv_checkpoints : nullptr;
+    out->qk_eps = f->qk_norm_eps;
+    out->gate = f->gate;
+    out->o_weight = f->o_norm_weight;
+    out->o_eps = f->o_norm_eps;
+    return KDA_SUCCESS;
+}
+
 struct ChunkPlan {
     int varlen, N, rows;
     int n_chunks_cap;
@@ -134,13 +193,18 @@ kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *a, void *stream)
             return fail(KDA_ERROR_INVALID_VALUE, "need checkpoint_every >= 1 and checkpoint_slots >= 1 (got %d, %d)",
                         a->checkpoint_every, a->checkpoint_slots);
     }
+    kda::FusionParams fp;
+    st = check_fusion(a->fusion, true, a->checkpoints != nullptr, a->dtype, pl.N, a->H, a->Dk, a->Dv, &fp);
+    if (st != KDA_SUCCESS) return st;
+    if (fp.conv_w > 0 || fp.gate)
+        return fail(KDA_ERROR_NOT_SUPPORTED, "the fused prologue / epilogue is not available in kda_chunk_fwd yet");
     if (pl.total > 0) {
         if (!a->workspace) return fail(KDA_ERROR_WORKSPACE, "workspace is NULL but %zu bytes are needed", pl.total);
         if (a->workspace_bytes < pl.total)
             return fail(KDA_ERROR_WORKSPACE, "workspace has %zu bytes, needs %zu", a->workspace_bytes, pl.total);
         if ((uintptr_t)a->workspace & 255u) return fail(KDA_ERROR_WORKSPACE, "workspace is not 256-byte aligned");
     }
-    if (!has_tokens && !a->final_state) {  // nothing observable to compute
+    if (!has_tokens && !a->final_state && !fp.conv_state_out) {  // nothing observable to compute
         g_err[0] = 0;
         return KDA_SUCCESS;
     }
@@ -158,6 +222,7 @@ kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *a, void *stream)
     p.ckpt = a->checkpoints;
     p.ckpt_every = a->checkpoints ? a->checkpoint_every : 0;
     p.ckpt_slots = a->checkpoints ? a->checkpoint_slots : 0;
+    p.f = fp;
     const hipError_t e = kda::launch_chunk_fwd(a->dtype == KDA_BF16, a->Dk, a->Dv, p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     g_err[0] = 0;
@@ -172,6 +237,9 @@ kda_status_t kda_recurrent_step(const kda_step_args_t *a, void *stream)
     if (a->N < 0 || a->H < 1) return fail(KDA_ERROR_INVALID_VALUE, "need N >= 0, H >= 1 (got N=%d H=%d)", a->N, a->H);
     // one workgroup per (sequence, head) must fit the launch grid
     if ((long long)a->N * a->H > 0x3fffffffLL) return fail(KDA_ERROR_NOT_SUPPORTED, "N*H too large");
+    kda::FusionParams fp;
+    st = check_fusion(a->fusion, false, false, a->dtype, a->N, a->H, a->Dk, a->Dv, &fp);
+    if (st != KDA_SUCCESS) return st;
     if (a->N == 0) { g_err[0] = 0; return KDA_SUCCESS; }
     const void *req[] = {a->q, a->k, a->v, a->g, a->beta, a->state, a->o};
     const char *nm[] = {"q", "k", "v", "g", "beta", "state", "o"};
@@ -191,6 +259,8 @@ kda_status_t kda_recurrent_step(const kda_step_args_t *a, void *stream)
     p.q = a->q; p.k = a->k; p.v = a->v; p.g = a->g; p.beta = a->beta;
     p.A_log = a->A_log; p.g_min = a->g_min; p.scale = a->scale;
     p.state = a->state; p.o = a->o;
+    p.q_r = nullptr;
+    p.f = fp;
     const hipError_t e = kda::launch_recurrent_replay(a->dtype == KDA_BF16, a->Dk, a->Dv, p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "kda_recurrent_step launch");
     g_err[0] = 0;
@@ -231,6 +301,13 @@ kda_status_t kda_recurrent_replay(const kda_replay_args_t *a, void *stream)
         if ((uintptr_t)a->beta_r & el) return fail(KDA_ERROR_INVALID_VALUE, "beta_r is not aligned to its element size");
         if (a->n_replay && ((uintptr_t)a->n_replay & 3u)) return fail(KDA_ERROR_INVALID_VALUE, "n_replay is not 4-byte aligned");
     }
+    kda::FusionParams fp;
+    st = check_fusion(a->fusion, false, false, a->dtype, a->N, a->H, a->Dk, a->Dv, &fp);
+    if (st != KDA_SUCCESS) return st;
+    if (fp.conv_w > 0 && a->T_replay > 0) {
+        if (!a->q_r) return fail(KDA_ERROR_INVALID_VALUE, "q_r is NULL (the fused prologue replays the query convolution)");
+        if (!aligned16(a->q_r)) return fail(KDA_ERROR_INVALID_VALUE, "q_r is not 16-byte aligned");
+    }
     if (a->N == 0 || a->T_replay + a->T_new == 0) { g_err[0] = 0; return KDA_SUCCESS; }
     kda::ReplayParams p;
     p.N = a->N; p.H = a->H;
@@ -240,6 +317,8 @@ kda_status_t kda_recurrent_replay(const kda_replay_args_t *a, void *stream)
     p.q = a->q; p.k = a->k; p.v = a->v; p.g = a->g; p.beta = a->beta;
     p.A_log = a->A_log; p.g_min = a->g_min; p.scale = a->scale;
     p.state = a->state; p.o = a->o;
+    p.q_r = (fp.conv_w > 0 && a->T_replay > 0) ? a->q_r : nullptr;
+    p.f = fp;
     const hipError_t e = kda::launch_recurrent_replay(a->dtype == KDA_BF16, a->Dk, a->Dv, p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "kda_recurrent_replay launch");
     g_err[0] = 0;

@@ -7,6 +7,19 @@
 
 namespace kda {
 
+// Layer prologue / epilogue fused around the recurrence (kda_layer_fusion_t).
+struct FusionParams {
+    int conv_w;                         // ShortConv width W (1..4), 0: no prologue
+    const float *conv_weight;           // [H, 2*Dk + Dv, W]
+    void *conv_state;                   // [N, H, W-1, 2*Dk + Dv] element type T, or null
+    void *conv_state_out;               // prefill: [N, H, W-1, 2*Dk + Dv] or null
+    void *conv_ckpt;                    // prefill: [N, ckpt_slots, H, W-1, 2*Dk + Dv] or null
+    float qk_eps;
+    const void *gate;                   // logits shaped like o, or null: no epilogue
+    const float *o_weight;              // [H, Dv]
+    float o_eps;
+};
+
 // Everything the three prefill kernels need, passed by value.
 struct PrefillParams {
     const void *q, *k, *v, *g, *beta;   // [rows, H, D] token-major, element type T
@@ -24,6 +37,7 @@ struct PrefillParams {
     int n_chunks_cap;
     float *ckpt;                        // [N, ckpt_slots, H, Dk, Dv] or null
     int ckpt_every, ckpt_slots;         // chunks between checkpoints, slots per sequence
+    FusionParams f;
 };
 
 // Bytes of one (head, chunk) workspace block; 0 if the combination is unsupported.
@@ -49,6 +63,8 @@ struct ReplayParams {
     float g_min, scale;
     float *state;                           // [N, H, Dk, Dv]
     void *o;                                // [N, T_new, H, Dv]
+    const void *q_r;                        // [N, T_replay, H, Dk] (prologue only)
+    FusionParams f;
 };
 
 hipError_t launch_recurrent_replay(int bf16, int Dk, int Dv, const ReplayParams &p, hipStream_t stream);

@@ -39,7 +39,19 @@ namespace kda {
 // with P_j k, P_j q and k / P_j formed once per row during staging, so the
 // per-element decay multiply disappears; the true state X * P is formed only
 // for the write-back and at the end of a block.
-template <typename T, int DK, int DV, int TB>
+//
+// FU: the layer's prologue (eq. (2)) and epilogue (eq. (6)) run in the same
+// pass, each switched on at run time.  Prologue: during staging the thread of
+// row r keeps the last three pre-activations of query and key channel r (and
+// the thread of column c those of value channel c) in registers, convolves,
+// applies Swish and stages the UNnormalised a_k, a_q with per-wave partial
+// sums of a_k^2 and a_q^2; L2Norm is a per-token scalar, so the token loop
+// multiplies the two reductions and the update by 1/|a_k| and 1/|a_q| instead
+// of a second staging pass.  The convolution state is written back with the
+// recurrent state's commit.  Epilogue: the block's outputs go to LDS; after
+// the block, each wave sums o~^2 over the head's d_v columns for each token and
+// the thread of column c writes Sigmoid(gate) * w_c * o~_c / rms.
+template <typename T, int DK, int DV, int TB, bool FU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void replay_kernel(ReplayParams p)
 {
     constexpr int NH = DK / 64;         // lanes per column
@@ -47,10 +59,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     constexpr int CPW = 64 / NH;        // columns per wave
     constexpr int NT = DV * NH;         // threads
     constexpr int NW = NT / 64;         // waves
-    static_assert(NH * RH == DK && NT % 64 == 0 && NT <= 256, "shape");
+    constexpr int CC = 2 * DK + DV;     // convolution channels per head
+    static_assert(NH * RH == DK && NT % 64 == 0 && NT <= 256 && NT >= DK && NT >= DV, "shape");
     __shared__ __align__(16) float s_kd[TB][DK], s_qd[TB][DK], s_ki[TB][DK];  // P_j k, P_j q, k / P_j
     __shared__ __align__(16) float s_pc[DK], s_pe[DK];    // P at the commit token, P at the block end
     __shared__ float s_v[TB][DV], s_b[TB], s_kqw[NW][TB];
+    constexpr int FT = FU ? TB : 1, FV = FU ? DV : 1, FW = FU ? NW : 1;
+    __shared__ float s_sk[FW][FT], s_sq[FW][FT];          // partial sums of a_k^2, a_q^2 (prologue)
+    __shared__ float s_o[FT][FV], s_gt[FT][FV];           // o~ and Sigmoid(gate) of the block (epilogue)
+    __shared__ float s_hist[FU ? 3 : 1][FU ? CC : 1];     // conv history between blocks (prologue)
 
     const int t = threadIdx.x, l = t & 63, w = t >> 6;
     const int hf = l / CPW;                       // which 64 rows of the column
@@ -82,6 +99,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     };
     const int r0h = hf * RH;                      // first row of this lane
 
+    // Prologue state: pre-activations 3, 2, 1 tokens back (slot 2 newest) of
+    // query / key channel t and value channel t, zero-padded below width 4,
+    // kept in LDS between blocks by the thread that owns the channels.
+    const bool pro = FU && p.f.conv_w > 0, epi = FU && p.f.gate != nullptr;
+    const int cw = pro ? p.f.conv_w : 1;
+    T *const cstate = (FU && cw > 1) ? (T *)p.f.conv_state + nh * (size_t)((cw - 1) * CC) : nullptr;
+    if constexpr (FU) {
+        if (pro) {
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {     // slot i holds state row i - 4 + cw (if any)
+                const int j = i - 4 + cw;
+                const bool in = cstate && j >= 0;
+                if (t < DK) {
+                    s_hist[i][t] = in ? to_f<T>(cstate[j * CC + t]) : 0.f;
+                    s_hist[i][DK + t] = in ? to_f<T>(cstate[j * CC + DK + t]) : 0.f;
+                }
+                if (t < DV) s_hist[i][2 * DK + t] = in ? to_f<T>(cstate[j * CC + 2 * DK + t]) : 0.f;
+            }
+        }
+    }
+
     for (int base = 0; base < n_tok; base += TB) {
         const int nb = min(TB, n_tok - base);
         const int jc = commit_at - 1 - base;      // commit token inside this block, if 0 <= jc < nb
@@ -90,26 +128,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
         {
             constexpr int RPT = (DK + NT - 1) / NT;  // staged rows per thread
             constexpr int CPT = (DV + NT - 1) / NT;  // staged value columns per thread
-            T gz[TB][RPT], kk[TB][RPT], qq[TB][RPT], vr[TB][CPT], bt[TB];
+            static_assert(!FU || (RPT == 1 && CPT == 1), "prologue staging assumes one row and one column per thread");
+            T gz[TB][RPT], kk[TB][RPT], qq[TB][RPT], vr[TB][CPT], bt[TB], gl[FT][CPT];
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
                 const int it = base + j;
                 const bool ok = j < nb, rep = it < n_rep;
                 const size_t row = ok ? row_of(it) : 0;
+                const T *qsrc = rep ? (pro ? (const T *)p.q_r : nullptr) : (const T *)p.q;
 #pragma unroll
                 for (int i = 0; i < RPT; ++i) {
                     const int r = t + i * NT;
                     const bool rk = ok && r < DK;
                     gz[j][i] = rk ? ((const T *)(rep ? p.g_r : p.g))[row * DK + r] : from_f<T>(0.f);
                     kk[j][i] = rk ? ((const T *)(rep ? p.k_r : p.k))[row * DK + r] : from_f<T>(0.f);
-                    qq[j][i] = (rk && !rep) ? ((const T *)p.q)[row * DK + r] : from_f<T>(0.f);
+                    qq[j][i] = (rk && qsrc) ? qsrc[row * DK + r] : from_f<T>(0.f);
                 }
 #pragma unroll
                 for (int i = 0; i < CPT; ++i) {
                     const int cc = t + i * NT;
                     vr[j][i] = (ok && cc < DV) ? ((const T *)(rep ? p.v_r : p.v))[row * DV + cc] : from_f<T>(0.f);
+                    if constexpr (FU)
+                        gl[j][i] = (epi && ok && !rep && cc < DV) ? ((const T *)p.f.gate)[row * DV + cc] : from_f<T>(0.f);
                 }
                 bt[j] = (ok && t == 0) ? ((const T *)(rep ? p.beta_r : p.beta))[row] : from_f<T>(0.f);
+            }
+            float wq[4] = {0.f, 0.f, 0.f, 0.f}, wk[4] = {0.f, 0.f, 0.f, 0.f}, wv[4] = {0.f, 0.f, 0.f, 0.f};
+            float hq[3] = {0.f, 0.f, 0.f}, hk[3] = {0.f, 0.f, 0.f}, hv[3] = {0.f, 0.f, 0.f};
+            // The thread index, opaque to the compiler inside this block: the
+            // prologue's per-thread addresses are recomputed here instead of being
+            // hoisted out of the block loop and kept live beside the state.
+            int tl = t;
+            if constexpr (FU) asm volatile("" : "+v"(tl));
+            if constexpr (FU) {
+                if (pro) {
+#pragma unroll
+                    for (int i = 0; i < 3; ++i) {
+                        if (tl < DK) {
+                            hq[i] = s_hist[i][tl];
+                            hk[i] = s_hist[i][DK + tl];
+                        }
+                        if (tl < DV) hv[i] = s_hist[i][2 * DK + tl];
+                    }
+                    // taps, newest last, zero-padded at the old end
+                    const float *wb = p.f.conv_weight + (size_t)h * CC * cw;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {  // tap i holds weight i - 4 + cw (if any)
+                        const int x = i - 4 + cw;
+                        if (x >= 0) {
+                            if (tl < DK) {
+                                wq[i] = wb[tl * cw + x];
+                                wk[i] = wb[(DK + tl) * cw + x];
+                            }
+                            if (tl < DV) wv[i] = wb[(2 * DK + tl) * cw + x];
+                        }
+                    }
+                }
             }
             float pr[RPT];                        // running product of alpha for this thread's rows
 #pragma unroll
@@ -117,32 +191,107 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
                 if (j >= nb) break;
-                float kq = 0.f;
+                float kq = 0.f, ssk = 0.f, ssq = 0.f;
+                float av = 0.f;
+                if constexpr (FU) {
+                    if (pro) {  // ShortConv + Swish (eq. (2)); conv history advances
+                        const float xq = to_f<T>(qq[j][0]), xk = to_f<T>(kk[j][0]), xv = to_f<T>(vr[j][0]);
+                        float cq = wq[3] * xq, ck = wk[3] * xk, cv = wv[3] * xv;
 #pragma unroll
-                for (int i = 0; i < RPT; ++i) {
-                    const int r = t + i * NT;
-                    if (r < DK) {
-                        float g = to_f<T>(gz[j][i]);
-                        g = p.A_log ? gate_from_logit(g, eA, p.g_min) : clamp_logdecay(g, p.g_min);
-                        const float kr = to_f<T>(kk[j][i]), qr = to_f<T>(qq[j][i]);
-                        pr[i] *= __expf(g);
-                        s_kd[j][r] = pr[i] * kr;
-                        s_qd[j][r] = pr[i] * qr;
-                        s_ki[j][r] = kr / pr[i];
-                        if (j == jc) s_pc[r] = pr[i];
-                        if (j == nb - 1) s_pe[r] = pr[i];
-                        kq += kr * qr;
+                        for (int i = 0; i < 3; ++i) {
+                            cq += wq[i] * hq[i];
+                            ck += wk[i] * hk[i];
+                            cv += wv[i] * hv[i];
+                        }
+                        hq[0] = hq[1]; hq[1] = hq[2]; hq[2] = xq;
+                        hk[0] = hk[1]; hk[1] = hk[2]; hk[2] = xk;
+                        hv[0] = hv[1]; hv[1] = hv[2]; hv[2] = xv;
+                        const float aq = cq / (1.f + __expf(-cq)), ak = ck / (1.f + __expf(-ck));
+                        av = cv / (1.f + __expf(-cv));
+                        if (j == jc && cstate) {  // committed: carry the last cw - 1 pre-activations
+#pragma unroll
+                            for (int i = 0; i < 3; ++i) {
+                                const int r = i - 4 + cw;
+                                if (r >= 0) {
+                                    if (tl < DK) {
+                                        cstate[r * CC + tl] = from_f<T>(hq[i]);
+                                        cstate[r * CC + DK + tl] = from_f<T>(hk[i]);
+                                    }
+                                    if (tl < DV) cstate[r * CC + 2 * DK + tl] = from_f<T>(hv[i]);
+                                }
+                            }
+                        }
+                        if (tl < DK) {
+                            float g = to_f<T>(gz[j][0]);
+                            g = p.A_log ? gate_from_logit(g, eA, p.g_min) : clamp_logdecay(g, p.g_min);
+                            pr[0] *= __expf(g);
+                            s_kd[j][tl] = pr[0] * ak;
+                            s_qd[j][tl] = pr[0] * aq;
+                            s_ki[j][tl] = ak / pr[0];
+                            if (j == jc) s_pc[tl] = pr[0];
+                            if (j == nb - 1) s_pe[tl] = pr[0];
+                            kq = ak * aq;
+                            ssk = ak * ak;
+                            ssq = aq * aq;
+                        }
+                    }
+                }
+                if (!pro) {
+#pragma unroll
+                    for (int i = 0; i < RPT; ++i) {
+                        const int r = tl + i * NT;
+                        if (r < DK) {
+                            float g = to_f<T>(gz[j][i]);
+                            g = p.A_log ? gate_from_logit(g, eA, p.g_min) : clamp_logdecay(g, p.g_min);
+                            const float kr = to_f<T>(kk[j][i]), qr = to_f<T>(qq[j][i]);
+                            pr[i] *= __expf(g);
+                            s_kd[j][r] = pr[i] * kr;
+                            s_qd[j][r] = pr[i] * qr;
+                            s_ki[j][r] = kr / pr[i];
+                            if (j == jc) s_pc[r] = pr[i];
+                            if (j == nb - 1) s_pe[r] = pr[i];
+                            kq += kr * qr;
+                        }
                     }
                 }
 #pragma unroll
                 for (int m = 32; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
                 if (l == 0) s_kqw[w][j] = kq;
+                if constexpr (FU) {
+                    if (pro) {
+#pragma unroll
+                        for (int m = 32; m >= 1; m >>= 1) {
+                            ssk += __shfl_xor(ssk, m);
+                            ssq += __shfl_xor(ssq, m);
+                        }
+                        if (l == 0) {
+                            s_sk[w][j] = ssk;
+                            s_sq[w][j] = ssq;
+                        }
+                    }
+                    if (epi && tl < DV) s_gt[j][tl] = 1.f / (1.f + __expf(-to_f<T>(gl[j][0])));
+                }
 #pragma unroll
                 for (int i = 0; i < CPT; ++i) {
-                    const int cc = t + i * NT;
-                    if (cc < DV) s_v[j][cc] = to_f<T>(vr[j][i]);
+                    const int cc = tl + i * NT;
+                    if (cc < DV) s_v[j][cc] = pro ? av : to_f<T>(vr[j][i]);
                 }
-                if (t == 0) s_b[j] = to_f<T>(bt[j]);
+                if (t == 0) {
+                    const float b = to_f<T>(bt[j]);
+                    s_b[j] = pro ? 1.f / (1.f + __expf(-b)) : b;
+                }
+            }
+            if constexpr (FU) {
+                if (pro) {
+#pragma unroll
+                    for (int i = 0; i < 3; ++i) {
+                        if (t < DK) {
+                            s_hist[i][tl] = hq[i];
+                            s_hist[i][DK + tl] = hk[i];
+                        }
+                        if (tl < DV) s_hist[i][2 * DK + tl] = hv[i];
+                    }
+                }
             }
         }
         __syncthreads();
@@ -153,6 +302,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
             const int it = base + j;
             const bool rep = it < n_rep;          // uniform across the workgroup
             const float *kd = &s_kd[j][r0h], *qd = &s_qd[j][r0h], *ki = &s_ki[j][r0h];
+            float nk = 1.f, nq = 1.f;             // 1 / |a_k|, 1 / |a_q| (prologue)
+            if constexpr (FU) {
+                if (pro) {
+                    float a = 0.f, b = 0.f;
+#pragma unroll
+                    for (int x = 0; x < NW; ++x) {
+                        a += s_sk[x][j];
+                        b += s_sq[x][j];
+                    }
+                    nk = rsqrtf(a + p.f.qk_eps);
+                    nq = rsqrtf(b + p.f.qk_eps);
+                }
+            }
             float pp = 0.f, rr = 0.f;
 #pragma unroll
             for (int g0 = 0; g0 < RH; g0 += GR) {
@@ -176,20 +338,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
                 pp += __shfl_xor(pp, 32);
                 if (!rep) rr += __shfl_xor(rr, 32);
             }
+            if constexpr (FU) {
+                pp *= nk;
+                rr *= nq;
+            }
             const float d = s_b[j] * (s_v[j][col] - pp);
             if (!rep && hf == 0) {
                 float kq = 0.f;
 #pragma unroll
                 for (int x = 0; x < NW; ++x) kq += s_kqw[x][j];
-                ((T *)p.o)[row_of(it) * DV + col] = from_f<T>(p.scale * (rr + d * kq));
+                if constexpr (FU) kq *= nk * nq;
+                const float ot = p.scale * (rr + d * kq);
+                if (FU && epi)
+                    s_o[FU ? j : 0][FU ? col : 0] = ot;
+                else
+                    ((T *)p.o)[row_of(it) * DV + col] = from_f<T>(ot);
             }
+            const float du = FU ? d * nk : d;     // k = a_k / |a_k| in the update
 #pragma unroll
             for (int g0 = 0; g0 < RH; g0 += GR) {
 #pragma unroll
                 for (int r = g0; r < g0 + GR; r += 4) {
                     const f32x4 i4 = *reinterpret_cast<const f32x4 *>(ki + r);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) st[r + e] += i4[e] * d;
+                    for (int e = 0; e < 4; ++e) st[r + e] += i4[e] * du;
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -201,6 +373,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
                     for (int e = 0; e < 4; ++e)
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, st[r + e] * p4[e]), srs,
                                                               lane_off, (r + e) * ROW, NT_AUX);
+                }
+            }
+        }
+        if constexpr (FU) {
+            if (epi && base + nb > n_rep) {       // eq. (6) over the block's new tokens
+                __syncthreads();                  // every column's o~ is in LDS
+                int te = t;
+                asm volatile("" : "+v"(te));      // as in staging: no hoisted addresses
+                const int le = te & 63;
+                const float wo = (te < DV) ? p.f.o_weight[(size_t)h * DV + te] : 0.f;
+                for (int j = max(n_rep - base, 0); j < nb; ++j) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int c = 0; c < DV; c += 64) ss += s_o[j][c + le] * s_o[j][c + le];
+#pragma unroll
+                    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+                    if (te < DV) {
+                        const float y = s_gt[j][te] * wo * s_o[j][te] * rsqrtf(ss * (1.f / DV) + p.f.o_eps);
+                        ((T *)p.o)[row_of(base + j) * DV + te] = from_f<T>(y);
+                    }
                 }
             }
         }
@@ -217,15 +409,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     }
 }
 
-template <typename T, int DK, int DV>
-static hipError_t launch_replay_t(const ReplayParams &p, hipStream_t stream)
+template <typename T, int DK, int DV, bool FU>
+static void launch_replay_tb(const ReplayParams &p, hipStream_t stream)
 {
     const unsigned grid = (unsigned)((size_t)p.N * p.H);
     const dim3 block(DV * (DK / 64));
     if (p.T_replay + p.T_new == 1)  // one token per sequence: the single decode step
-        hipLaunchKernelGGL((replay_kernel<T, DK, DV, 1>), dim3(grid), block, 0, stream, p);
+        hipLaunchKernelGGL((replay_kernel<T, DK, DV, 1, FU>), dim3(grid), block, 0, stream, p);
     else
-        hipLaunchKernelGGL((replay_kernel<T, DK, DV, 8>), dim3(grid), block, 0, stream, p);
+        hipLaunchKernelGGL((replay_kernel<T, DK, DV, 8, FU>), dim3(grid), block, 0, stream, p);
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_replay_t(const ReplayParams &p, hipStream_t stream)
+{
+    if (p.f.conv_w > 0 || p.f.gate)
+        launch_replay_tb<T, DK, DV, true>(p, stream);
+    else
+        launch_replay_tb<T, DK, DV, false>(p, stream);
     return hipGetLastError();
 }
 

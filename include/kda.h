@@ -14,6 +14,8 @@
  * (§5.4.2, "KDA" paragraph: the decode state is updated in place every step);
  * kda_recurrent_replay runs a speculative-decoding window (replayed accepted
  * tokens plus new tokens) in one pass over the in-place state (same paragraph).
+ * Each entry point can also apply the layer's input prologue (eq. (2)) and
+ * output epilogue (eq. (6)) inside its kernels; see kda_layer_fusion_t.
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; all tensors are
@@ -63,6 +65,63 @@ typedef enum {
     KDA_ERROR_WORKSPACE = 3,       /* workspace missing or smaller than required */
     KDA_ERROR_HIP = 4              /* a HIP runtime call or kernel launch failed */
 } kda_status_t;
+
+/*
+ * Optional fusion of the layer around the recurrence ("Kimi K3 Technical
+ * Report", §2.1.1 eqs. (2) and (6); §5.4.2 describes the decode kernel as one
+ * fused loop over short convolution, input normalisation, gating, the
+ * recurrence and output normalisation).  The dense projections (W x products,
+ * the low-rank decay projection and W_o) stay with the caller.
+ *
+ * Prologue (eq. (2)), on when conv_width >= 1.  Then q, k, v hold the
+ * projections W_q x, W_k x, W_v x BEFORE the convolution and beta holds the
+ * logits W_beta x; per head and token the kernels form
+ *   q = L2Norm(Swish(ShortConv(W_q x))),  k likewise,  v = Swish(ShortConv(W_v x)),
+ *   beta = Sigmoid(W_beta x),
+ * with Swish(x) = x Sigmoid(x) (§2.3.2) and L2Norm(y) = y / sqrt(sum y^2 + qk_norm_eps)
+ * over the head's Dk channels.  ShortConv is a causal depthwise convolution over
+ * time with no bias: channel c of token t is
+ *   sum_{i < W} conv_weight[h][c][i] * x[t - (W - 1) + i][c],
+ * the W - 1 positions before a sequence's first token read from conv_state.
+ * Channels per head: Dk query channels, then Dk key channels, then Dv value
+ * channels (C = 2*Dk + Dv).  g (log-decays or logits z, with A_log) is used
+ * as without the prologue.
+ *   conv_weight : [H, C, W] float32, 16-byte aligned.
+ *   conv_state  : [N, H, W - 1, C] elements of the call's dtype: the
+ *                 pre-activations of the W - 1 tokens before the first one
+ *                 (oldest first).
+ *     kda_chunk_fwd:        read only; NULL = zeros (fresh sequences).
+ *     kda_recurrent_step / kda_recurrent_replay: required when W > 1; read and
+ *                 overwritten IN PLACE at the commit point with the W - 1
+ *                 pre-activations before it (replayed tokens included; left
+ *                 untouched when nothing is committed), like the state.
+ *   conv_state_out : kda_chunk_fwd only (NULL elsewhere): [N, H, W - 1, C],
+ *                 each sequence's last W - 1 pre-activations (older rows
+ *                 from conv_state when a sequence is shorter), or NULL.  It
+ *                 must not overlap conv_state.
+ *   conv_checkpoints : kda_chunk_fwd only, with checkpoints set: [N, slots, H,
+ *                 W - 1, C]; slot j receives the convolution state at the
+ *                 position of checkpoint slot j (what resuming from that
+ *                 checkpoint needs as conv_state), or NULL.
+ * Epilogue (eq. (6) without W_o), on when gate is non-NULL: o receives
+ *   y = Sigmoid(gate) * o_norm_weight[h] * o~ / sqrt(mean(o~^2) + o_norm_eps)
+ * per head and token (mean over the Dv channels of the recurrence output o~).
+ *   gate          : logits W_g x, shaped like o, in the call's dtype.
+ *   o_norm_weight : [H, Dv] float32, required with gate.
+ * Both epsilons must be >= 0.  A NULL fusion pointer (or conv_width = 0 and
+ * gate = NULL) leaves every entry point exactly as documented above it.
+ */
+typedef struct {
+    int32_t conv_width;            /* W in 1..4, or 0: no prologue */
+    const float *conv_weight;
+    void *conv_state;
+    void *conv_state_out;
+    void *conv_checkpoints;
+    float qk_norm_eps;
+    const void *gate;              /* NULL: no epilogue */
+    const float *o_norm_weight;
+    float o_norm_eps;
+} kda_layer_fusion_t;
 
 /* Chunk size of the chunkwise-parallel form and its sub-tile size. */
 #define KDA_CHUNK 64
@@ -120,6 +179,7 @@ typedef struct {
     float *checkpoints;            /* optional prefix-state checkpoints, see above */
     int32_t checkpoint_every;      /* chunks of KDA_CHUNK tokens between checkpoints */
     int32_t checkpoint_slots;      /* capacity per sequence */
+    const kda_layer_fusion_t *fusion;   /* optional prologue / epilogue, or NULL */
 } kda_chunk_fwd_args_t;
 
 /* Workspace bytes kda_chunk_fwd needs for these shapes (pointers are not read).
@@ -146,6 +206,7 @@ typedef struct {
     float scale;
     float *state;
     void *o;
+    const kda_layer_fusion_t *fusion;   /* optional prologue / epilogue, or NULL */
 } kda_step_args_t;
 
 KDA_API kda_status_t kda_recurrent_step(const kda_step_args_t *args, void *stream);
@@ -178,6 +239,9 @@ KDA_API kda_status_t kda_recurrent_step(const kda_step_args_t *args, void *strea
  * T_new; the replay tensors may be NULL when T_replay = 0 and the new-window
  * tensors when T_new = 0.  Dk, Dv, dtype, A_log / g and alignment as for
  * kda_recurrent_step; the state must not alias any other argument.
+ * With the fused prologue the replayed window also needs its query
+ * projections, q_r : [N, T_replay, H, Dk] (the query convolution runs through
+ * the replayed tokens); q_r is ignored otherwise.
  */
 typedef struct {
     int32_t N, H, Dk, Dv;
@@ -191,6 +255,8 @@ typedef struct {
     float scale;
     float *state;
     void *o;
+    const void *q_r;                    /* replayed query projections (fused prologue only) */
+    const kda_layer_fusion_t *fusion;   /* optional prologue / epilogue, or NULL */
 } kda_replay_args_t;
 
 KDA_API kda_status_t kda_recurrent_replay(const kda_replay_args_t *args, void *stream);

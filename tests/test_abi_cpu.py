@@ -235,3 +235,62 @@ def test_binding_shape_checks():
         _same_lead(q, q, v, q, b[:, :4], None, 2)
     with pytest.raises(ValueError, match="A_log"):
         _same_lead(q, q, v, q, b, torch.zeros(3), 2)
+
+
+def _fusion(**over):
+    f = kda.LayerFusion()
+    f.conv_width, f.conv_weight, f.conv_state, f.qk_norm_eps = 4, 0x30000, 0x40000, 1e-6
+    for key, val in over.items():
+        setattr(f, key, val)
+    return f
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(conv_width=5), 2, "conv_width=5"),
+    (dict(conv_width=-1), 2, "conv_width=-1"),
+    (dict(conv_weight=None), 1, "conv_weight is NULL"),
+    (dict(conv_weight=0x30004), 1, "conv_weight is not 16-byte aligned"),
+    (dict(conv_state=None), 1, "conv_state is NULL"),
+    (dict(conv_state_out=0x50000), 1, "kda_chunk_fwd only"),
+    (dict(conv_checkpoints=0x50000), 1, "kda_chunk_fwd only"),
+    (dict(qk_norm_eps=-1.0), 1, "qk_norm_eps"),
+    (dict(conv_width=0), 1, "conv_width = 0"),
+    (dict(gate=0x60000, o_norm_weight=None), 1, "o_norm_weight is NULL"),
+    (dict(gate=0x60008, o_norm_weight=0x70000), 1, "gate is not 16-byte aligned"),
+    (dict(gate=0x60000, o_norm_weight=0x70000, o_norm_eps=-2.0), 1, "o_norm_eps"),
+])
+def test_decode_fusion_rejects_before_launch(lib, over, status, msg):
+    f = _fusion(**over)
+    a = kda.StepArgs()
+    a.N, a.H, a.Dk, a.Dv, a.dtype = 4, 2, 128, 128, kda.KDA_BF16
+    for name in ("q", "k", "v", "g", "beta", "state", "o"):
+        setattr(a, name, 0x10000)
+    a.g_min, a.scale = -5.0, 1.0
+    a.fusion = ctypes.pointer(f)
+    assert lib.kda_recurrent_step(ctypes.byref(a), None) == status
+    assert msg in lib.kda_last_error_message().decode()
+    r = _replay_args()
+    r.fusion = ctypes.pointer(f)
+    r.q_r = 0x10000
+    assert lib.kda_recurrent_replay(ctypes.byref(r), None) == status
+    assert msg in lib.kda_last_error_message().decode()
+
+
+def test_replay_fusion_needs_query_projections(lib):
+    f = _fusion()
+    r = _replay_args()
+    r.fusion = ctypes.pointer(f)
+    assert lib.kda_recurrent_replay(ctypes.byref(r), None) == 1
+    assert "q_r is NULL" in lib.kda_last_error_message().decode()
+    r = _replay_args(T_replay=0, k_r=None, v_r=None, g_r=None, beta_r=None, n_replay=None, N=0)
+    r.fusion = ctypes.pointer(f)                     # no replayed tokens: q_r not needed
+    assert lib.kda_recurrent_replay(ctypes.byref(r), None) == 0
+
+
+def test_decode_fusion_width_one_needs_no_state(lib):
+    """W = 1 carries no convolution state (checked on N = 0: nothing launched)."""
+    f = _fusion(conv_width=1, conv_state=None)
+    a = kda.StepArgs()
+    a.N, a.H, a.Dk, a.Dv, a.dtype, a.g_min = 0, 2, 128, 128, kda.KDA_BF16, -5.0
+    a.fusion = ctypes.pointer(f)
+    assert lib.kda_recurrent_step(ctypes.byref(a), None) == 0

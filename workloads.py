@@ -245,3 +245,36 @@ def make_spec_decode(w: Workload, device="cpu", N: int | None = None, H: int | N
                         n_replay=n_rep.to(device), q=new["q"], k=new["k"], v=new["v"], z=new["z"],
                         beta=new["beta"]))
     return dict(state=state, A_log=A.float(), calls=out, g_min=G_MIN)
+
+
+def make_layer(w: Workload, device="cpu", N: int | None = None, T: int | None = None, H: int | None = None,
+               conv_width: int = 4, seed_offset: int = 0):
+    """Inputs of the layer around the core (eq. (2) prologue, eq. (6) epilogue)
+    on the workload's shapes: token-major [N, T, H, .] tensors in the workload
+    dtype.  The dense projections are not modelled: their outputs are drawn
+    directly.  Returns dict with
+      q_pre, k_pre, z [N, T, H, Dk]; v_pre, gate [N, T, H, Dv]; beta_logit [N, T, H]
+          (projections W x ~ N(0, 1), decay logits z ~ N(0, 1), gate logits ~ N(0, 1));
+      conv_weight [H, 2*Dk + Dv, W] fp32 (taps ~ N(0, 0.5^2));
+      conv_state [N, H, W-1, 2*Dk + Dv] (pre-activations ~ N(0, 1));
+      o_norm_weight [H, Dv] fp32 (1 + N(0, 0.1^2));
+      state [N, H, Dk, Dv] fp32 (N(0, h0_std^2)); A_log [H] (U(-a, a)); g_min.
+    """
+    N = N or w.B
+    T = w.T if T is None else T
+    H = H or w.H
+    gen = _gen(w.seed + 1000 + seed_offset, device)
+    dt = w.dtype
+    C = 2 * w.Dk + w.Dv
+    nrm = lambda *shape: _normal(shape, gen, device)
+    out = dict(
+        q_pre=nrm(N, T, H, w.Dk).to(dt), k_pre=nrm(N, T, H, w.Dk).to(dt), v_pre=nrm(N, T, H, w.Dv).to(dt),
+        z=nrm(N, T, H, w.Dk).to(dt), beta_logit=nrm(N, T, H).to(dt), gate=nrm(N, T, H, w.Dv).to(dt),
+        conv_weight=nrm(H, C, conv_width) * 0.5,
+        conv_state=nrm(N, H, conv_width - 1, C).to(dt),
+        o_norm_weight=1.0 + 0.1 * nrm(H, w.Dv),
+        state=nrm(N, H, w.Dk, w.Dv) * w.h0_std,
+        A_log=(torch.rand((H,), generator=gen, device=device) * 2 - 1) * w.A_uniform if w.A_uniform > 0
+        else torch.zeros((H,), device=device),
+        g_min=G_MIN)
+    return out
