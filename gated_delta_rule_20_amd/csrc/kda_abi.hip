@@ -196,8 +196,6 @@ kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *a, void *stream)
     kda::FusionParams fp;
     st = check_fusion(a->fusion, true, a->checkpoints != nullptr, a->dtype, pl.N, a->H, a->Dk, a->Dv, &fp);
     if (st != KDA_SUCCESS) return st;
-    if (fp.conv_w > 0 || fp.gate)
-        return fail(KDA_ERROR_NOT_SUPPORTED, "the fused prologue / epilogue is not available in kda_chunk_fwd yet");
     if (pl.total > 0) {
         if (!a->workspace) return fail(KDA_ERROR_WORKSPACE, "workspace is NULL but %zu bytes are needed", pl.total);
         if (a->workspace_bytes < pl.total)

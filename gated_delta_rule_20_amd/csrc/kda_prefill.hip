@@ -213,6 +213,8 @@ template <typename T, int DK, int DV> struct RawIn {
     vu v[HT];
     T beta;
     float alog;
+    ku hk[3], hq[3];   // prologue: pre-activations of the 3 tokens before the segment (oldest first)
+    vu hv[3];
 };
 
 template <typename T, int DK, int DV>
@@ -265,8 +267,14 @@ template <typename V> __device__ __forceinline__ V buf_load(__amdgpu_buffer_rsrc
         return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, 0));
 }
 
-// Token range of chunk c; false if c is past the last chunk (packed tail).
-__device__ __forceinline__ bool locate_chunk(const PrefillParams &p, int c, int &tok0, int &len)
+// Where chunk c sits: its first token, token count, sequence, index inside
+// the sequence and the sequence's length.  False if c is past the last chunk
+// (packed tail).
+struct ChunkLoc {
+    int tok0, len, sq, lc, slen;
+};
+
+__device__ __forceinline__ bool locate_chunk(const PrefillParams &p, int c, ChunkLoc &cl)
 {
     if (p.varlen) {
         if (c >= ld_uniform(p.chunk_off, p.N)) return false;
@@ -275,34 +283,114 @@ __device__ __forceinline__ bool locate_chunk(const PrefillParams &p, int c, int 
             const int mid = (lo + hi + 1) >> 1;
             if (ld_uniform(p.chunk_off, mid) <= c) lo = mid; else hi = mid - 1;
         }
-        tok0 = ld_uniform(p.cu, lo) + (c - ld_uniform(p.chunk_off, lo)) * CHUNK;
-        len = min(CHUNK, ld_uniform(p.cu, lo + 1) - tok0);
+        const int start = ld_uniform(p.cu, lo);
+        cl.sq = lo;
+        cl.lc = c - ld_uniform(p.chunk_off, lo);
+        cl.slen = ld_uniform(p.cu, lo + 1) - start;
+        cl.tok0 = start + cl.lc * CHUNK;
+        cl.len = min(CHUNK, cl.slen - cl.lc * CHUNK);
     } else {
         const int cps = (p.T + CHUNK - 1) / CHUNK;
-        const int s = c / cps, lc = c - s * cps;
-        tok0 = s * p.T + lc * CHUNK;
-        len = min(CHUNK, p.T - lc * CHUNK);
+        cl.sq = c / cps;
+        cl.lc = c - cl.sq * cps;
+        cl.slen = p.T;
+        cl.tok0 = cl.sq * p.T + cl.lc * CHUNK;
+        cl.len = min(CHUNK, p.T - cl.lc * CHUNK);
     }
     return true;
 }
 
 // Next valid item at or after i (stride gridDim.x); items run chunk-major
 // from the last chunk down.  Returns false when the walk is done.
-__device__ __forceinline__ bool next_item(const PrefillParams &p, int &i, int &c, int &h, int &tok0, int &len)
+__device__ __forceinline__ bool next_item(const PrefillParams &p, int &i, int &c, int &h, ChunkLoc &cl)
 {
     const int n_items = p.n_chunks_cap * p.H;
     for (; i < n_items; i += gridDim.x) {
         const int ci = i / p.H;
         h = i - ci * p.H;
         c = p.n_chunks_cap - 1 - ci;
-        if (locate_chunk(p, c, tok0, len)) return true;
+        if (locate_chunk(p, c, cl)) return true;
     }
     return false;
 }
 
+// Prologue: the pre-activations of the 3 tokens before the wave's segment
+// (token tb of item cl, head h), oldest first, into in.hq / hk / hv.  They
+// come from the token arrays when they lie in the sequence, from conv_state
+// (row j = slot - 4 + W) at a sequence start, and are zero past the filter,
+// without conv_state, or for a segment past the chunk's end.
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void load_hist(RawIn<T, DK, DV> &in, const PrefillParams &p, const ChunkLoc &cl, bool have,
+                                          int h, int tb, int l)
+{
+    using R = RawIn<T, DK, DV>;
+    typedef typename R::ku ku;
+    typedef typename R::vu vu;
+    constexpr int EL = (int)sizeof(T), C = 2 * DK + DV;
+    const int rowk = p.H * DK * EL, rowv = p.H * DV * EL;
+    const bool seg = have && tb < cl.len;
+    const bool from_state = tb == 0 && cl.lc == 0;
+    if (from_state) {
+        const bool st = seg && p.f.conv_state && p.f.conv_w > 1;
+        const int W = p.f.conv_w;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((const T *)(st ? p.f.conv_state : p.q) + (st ? ((size_t)cl.sq * p.H + h) * (W - 1) * C : 0)), 0,
+            st ? (W - 1) * C * EL : 0, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int j = i - 4 + W;
+            const int ro = j >= 0 ? j * C * EL : 0x40000000;  // past the record count: reads as zero
+            in.hq[i] = buf_load<ku>(rs, ro + R::CPT * l * EL);
+            in.hk[i] = buf_load<ku>(rs, ro + (DK + R::CPT * l) * EL);
+            in.hv[i] = buf_load<vu>(rs, ro + (2 * DK + R::CPV * l) * EL);
+        }
+    } else {
+        // tokens tb - 3 .. tb - 1 of the same sequence (the previous chunk's tail when tb = 0)
+        const size_t row0 = seg ? (size_t)(cl.tok0 + tb - 3) * p.H + h : 0;
+        const int reck = seg ? 2 * rowk + DK * EL : 0, recv = seg ? 2 * rowv + DV * EL : 0;
+        const __amdgpu_buffer_rsrc_t rsq = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.q + row0 * DK), 0, reck, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.k + row0 * DK), 0, reck, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.v + row0 * DV), 0, recv, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            in.hq[i] = buf_load<ku>(rsq, i * rowk + R::CPT * l * EL);
+            in.hk[i] = buf_load<ku>(rsk, i * rowk + R::CPT * l * EL);
+            in.hv[i] = buf_load<vu>(rsv, i * rowv + R::CPV * l * EL);
+        }
+    }
+}
+
+// Sums each of 16 per-lane values over the wave's 64 lanes (a transposed
+// butterfly: each exchange halves the values a lane carries, 17 lane swaps in
+// all instead of 96) and returns total i, uniform, in out[i].
+__device__ __forceinline__ void wave_sum16(const float (&v)[16], float (&out)[16], int l)
+{
+    float a[8], b[4], c[2];
+    const bool b5 = l & 32, b4 = l & 16, b3 = l & 8, b2 = l & 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (b5 ? v[i + 8] : v[i]) + __shfl_xor(b5 ? v[i] : v[i + 8], 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = (b4 ? a[i + 4] : a[i]) + __shfl_xor(b4 ? a[i] : a[i + 4], 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) c[i] = (b3 ? b[i + 2] : b[i]) + __shfl_xor(b3 ? b[i] : b[i + 2], 8);
+    float d = (b2 ? c[1] : c[0]) + __shfl_xor(b2 ? c[0] : c[1], 4);  // value 8 b5 + 4 b4 + 2 b3 + b2
+    d += __shfl_xor(d, 2);
+    d += __shfl_xor(d, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d), 4 * i));
+}
+
 // ZM: decay logits z with the eq. (5) gate (A_log given), else log-decays g;
 // a template parameter so the elementwise pass carries no per-element branch.
-template <typename T, int DK, int DV, bool ZM>
+//
+// PRO: the layer's input prologue (eq. (2)) runs first in P1: each wave
+// convolves its 8 tokens with the 3 pre-activations before them (ShortConv,
+// taps zero-padded to width 4), applies Swish, zeroes tokens past the chunk
+// (the convolution would otherwise give them values), L2-normalises q and k
+// with one 16-value wave reduction, and applies Sigmoid to the beta logits.
+// The last chunk of a sequence writes its convolution state, checkpoint
+// chunks their convolution checkpoints.
+template <typename T, int DK, int DV, bool ZM, bool PRO>
 __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 {
     using BL = Block<T, DK, DV>;
@@ -319,13 +407,16 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
     const int ch0 = CPT * l;  // first channel of this lane in the elementwise phase
     const int m0 = w & 3, hf = w >> 2, tb = seg_base(w);  // elementwise: tile, half, first token
 
-    int i = blockIdx.x, c, h, tok0, len;
-    bool have = next_item(p, i, c, h, tok0, len);
+    int i = blockIdx.x, c, h;
+    ChunkLoc cl{};
+    bool have = next_item(p, i, c, h, cl);
     R raw;
-    if (have) load_raw(raw, p, tok0, len, h, w, l);
+    if (have) load_raw(raw, p, cl.tok0, cl.len, h, w, l);
+    if constexpr (PRO) load_hist(raw, p, cl, have, h, tb, l);
     __builtin_amdgcn_s_waitcnt(0);
 
     while (have) {
+        const int tok0 = cl.tok0, len = cl.len;
         char *blkb = p.blocks + ((size_t)h * p.n_chunks_cap + c) * BL::BYTES;
         T *blk = reinterpret_cast<T *>(blkb);
         float *gamma_out = reinterpret_cast<float *>(blkb + BL::GAMMA_BYTE);
@@ -336,8 +427,10 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         // wait here holds back on the previous item's result stores.
         // The next item's raw inputs are loaded into each raw register right after
         // its last use below, so the loads issue between this item's VALU work.
-        int i2 = i + gridDim.x, c2 = 0, h2 = 0, tok2 = 0, len2 = 0;
-        const bool have2 = next_item(p, i2, c2, h2, tok2, len2);
+        int i2 = i + gridDim.x, c2 = 0, h2 = 0;
+        ChunkLoc cl2{};
+        const bool have2 = next_item(p, i2, c2, h2, cl2);
+        const int tok2 = cl2.tok0, len2 = cl2.len;
         // The next item's rows of this wave through buffer descriptors: base at its
         // first token (uniform), lane offset plus token offset in one VGPR shared by
         // g, k and q, and a record count that ends at the last valid token, so tokens
@@ -352,6 +445,99 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         const __amdgpu_buffer_rsrc_t rsq = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.q + row0 * DK), 0, reck, 0x00020000);
         const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.v + row0 * DV), 0, recv, 0x00020000);
         const int offk = ch0 * (int)sizeof(T), offv = CPV * l * (int)sizeof(T);
+        // ---- P1 prologue (eq. (2)): q, k, v activations of the wave's tokens ----
+        float ka[PRO ? HT : 1][CPT], qa[PRO ? HT : 1][CPT], va[PRO ? HT : 1][CPV];
+        if constexpr (PRO) {
+            constexpr int C = 2 * DK + DV;
+            const int W = p.f.conv_w;
+            float wq[CPT][4], wk[CPT][4], wv[CPV][4];  // taps, newest last, zero-padded at the old end
+            const float *wb = p.f.conv_weight + (size_t)h * C * W;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int xw = e - 4 + W;
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    wq[cc][e] = xw >= 0 ? wb[(ch0 + cc) * W + xw] : 0.f;
+                    wk[cc][e] = xw >= 0 ? wb[(DK + ch0 + cc) * W + xw] : 0.f;
+                }
+#pragma unroll
+                for (int cv = 0; cv < CPV; ++cv) wv[cv][e] = xw >= 0 ? wb[(2 * DK + CPV * l + cv) * W + xw] : 0.f;
+            }
+            auto swish = [](float u) { return u * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-LOG2E * u)); };
+            float ssq[16];  // per token: sum of a_k^2 (0..7), a_q^2 (8..15) over this lane's channels
+#pragma unroll
+            for (int r0 = 0; r0 < HT; ++r0) {
+                const bool ok = tb + r0 < len;
+                ssq[r0] = 0.f;
+                ssq[HT + r0] = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    float cq = 0.f, ck = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {  // token r0 - 3 + e; negative: history slot
+                        const int rr = r0 - 3 + e;
+                        cq += wq[cc][e] * to_f<T>(rr < 0 ? raw.hq[rr + 3][cc] : raw.q[rr < 0 ? 0 : rr][cc]);
+                        ck += wk[cc][e] * to_f<T>(rr < 0 ? raw.hk[rr + 3][cc] : raw.k[rr < 0 ? 0 : rr][cc]);
+                    }
+                    qa[r0][cc] = ok ? swish(cq) : 0.f;
+                    ka[r0][cc] = ok ? swish(ck) : 0.f;
+                    ssq[r0] += ka[r0][cc] * ka[r0][cc];
+                    ssq[HT + r0] += qa[r0][cc] * qa[r0][cc];
+                }
+#pragma unroll
+                for (int cv = 0; cv < CPV; ++cv) {
+                    float cx = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int rr = r0 - 3 + e;
+                        cx += wv[cv][e] * to_f<T>(rr < 0 ? raw.hv[rr + 3][cv] : raw.v[rr < 0 ? 0 : rr][cv]);
+                    }
+                    va[r0][cv] = ok ? swish(cx) : 0.f;
+                }
+            }
+            float tot[16];
+            wave_sum16(ssq, tot, l);
+#pragma unroll
+            for (int r0 = 0; r0 < HT; ++r0) {
+                const float nk = rsqrtf(tot[r0] + p.f.qk_eps), nq = rsqrtf(tot[HT + r0] + p.f.qk_eps);
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    ka[r0][cc] *= nk;
+                    qa[r0][cc] *= nq;
+                }
+            }
+            // Convolution state after the sequence (last chunk) and at checkpoint
+            // positions: the pre-activations of chunk positions q0 .. q0 + W - 2; a
+            // position before the chunk (q < 0) is history slot q + 3 of wave tb = 0.
+            auto put_rows = [&](T *dst, int q0) {
+                for (int j = 0; j < W - 1; ++j) {
+                    const int qp = q0 + j;
+                    const bool mine = (qp < 0) ? (tb == 0) : (qp >= tb && qp < tb + HT);
+                    if (!mine) continue;
+                    const int sl = qp < 0 ? qp + 3 : 0, rr = qp < 0 ? 0 : qp - tb;
+                    ku xq = raw.q[0], xk = raw.k[0];
+                    typename R::vu xv = raw.v[0];
+#pragma unroll
+                    for (int e = 0; e < HT; ++e)
+                        if (qp >= 0 && rr == e) { xq = raw.q[e]; xk = raw.k[e]; xv = raw.v[e]; }
+#pragma unroll
+                    for (int e = 0; e < 3; ++e)
+                        if (qp < 0 && sl == e) { xq = raw.hq[e]; xk = raw.hk[e]; xv = raw.hv[e]; }
+                    *reinterpret_cast<ku *>(dst + j * C + ch0) = xq;
+                    *reinterpret_cast<ku *>(dst + j * C + DK + ch0) = xk;
+                    *reinterpret_cast<typename R::vu *>(dst + j * C + 2 * DK + CPV * l) = xv;
+                }
+            };
+            if (p.f.conv_state_out && cl.lc * CHUNK + len == cl.slen)
+                put_rows((T *)p.f.conv_state_out + ((size_t)cl.sq * p.H + h) * (W - 1) * C, len - (W - 1));
+            if (p.f.conv_ckpt && p.ckpt_every > 0 && (cl.lc + 1) % p.ckpt_every == 0) {
+                const int slot = (cl.lc + 1) / p.ckpt_every - 1;
+                if (slot < p.ckpt_slots && (cl.lc + 1) * CHUNK < cl.slen)
+                    put_rows((T *)p.f.conv_ckpt + (((size_t)cl.sq * p.ckpt_slots + slot) * p.H + h) * (W - 1) * C,
+                             CHUNK - (W - 1));
+            }
+            load_hist(raw, p, cl2, have2, h2, tb, l);  // the next item's history (registers now free)
+        }
         float lam2[HT][CPT];  // (lam_r - B_m) log2(e) for this wave's tokens (tile m = w % 4)
         {
             const float cz = -__expf(raw.alog) * LOG2E;  // exp(-e^A z) = exp2(cz z)
@@ -373,7 +559,10 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             }
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) sm.tot[2 * m0 + hf][ch0 + cc] = run[cc];
-            if (l < HT) sm.beta[tb + l] = to_f<T>(raw.beta);
+            if (l < HT) {
+                const float b = to_f<T>(raw.beta);  // PRO: the logit W_beta x
+                sm.beta[tb + l] = PRO ? (tb + l < len ? 1.f / (1.f + __expf(-b)) : 0.f) : b;
+            }
         }
         {
             const int bt = tb + l;
@@ -413,8 +602,8 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 ku kr_, qr_, kc_, ke_, kx1_, kx2_;
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) {
-                    const float kv = to_f<T>(raw.k[r0][cc]);
-                    const float qv = p.scale * to_f<T>(raw.q[r0][cc]);
+                    const float kv = PRO ? ka[PRO ? r0 : 0][cc] : to_f<T>(raw.k[r0][cc]);
+                    const float qv = p.scale * (PRO ? qa[PRO ? r0 : 0][cc] : to_f<T>(raw.q[r0][cc]));
                     const float eR = __builtin_amdgcn_exp2f(lam2[r0][cc]);        // exp(lam_r - B_w) <= 1
                     const float eC = __builtin_amdgcn_rcpf(eR);  // exp(B_w - lam_r) <= e^80
                     const float kr = kv * eR, qr = qv * eR, kcs = kv * eC, kce = kcs * eT[cc];
@@ -454,7 +643,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             for (int cv = 0; cv < CPV; ++cv) {
                 tok8 col;
 #pragma unroll
-                for (int r = 0; r < HT; ++r) col[r] = raw.v[r][cv];
+                for (int r = 0; r < HT; ++r) col[r] = PRO ? from_f<T>(va[PRO ? r : 0][cv]) : raw.v[r][cv];
                 *reinterpret_cast<tok8 *>(&sm.VT[CPV * l + cv][tb]) = col;
             }
 #pragma unroll
@@ -641,7 +830,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             }
         }
         lds_barrier();  // LDS is reused by the next item
-        i = i2; c = c2; h = h2; tok0 = tok2; len = len2;
+        i = i2; c = c2; h = h2; cl = cl2;
         have = have2;
     }
 }
@@ -910,30 +1099,90 @@ static long intra_grid()
     return n;
 }
 
+// -----------------------------------------------------------------------------
+// Output epilogue (eq. (6) without W_o), in place on o after the chain:
+// o <- Sigmoid(gate) * w_h * o / sqrt(mean(o^2) + eps) per (token, head) row.
+// The chain holds 16 of a head's d_v columns per workgroup, so the per-row
+// mean square needs this separate, bandwidth-bound pass: each lane moves 16
+// bytes of o and of the gate, a row spans DV / VPL lanes and is reduced with
+// lane swaps inside that group.
+template <typename T, int DV>
+__global__ __launch_bounds__(256) void gate_norm_kernel(T *o, const T *gate, const float *wgt, int H, long rows,
+                                                        float eps)
+{
+    constexpr int VPL = 16 / (int)sizeof(T), LPR = DV / VPL, RPW = 64 / LPR;
+    typedef typename Vec<T, VPL>::type vec;
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const long row = ((long)blockIdx.x * 4 + w) * RPW + l / LPR;
+    const int c0 = (l % LPR) * VPL;
+    const bool ok = row < rows;                    // uniform within a row's lane group
+    const size_t off = (size_t)(ok ? row : 0) * DV + c0;
+    vec ov = *reinterpret_cast<const vec *>(o + off), gv = *reinterpret_cast<const vec *>(gate + off);
+    const int h = (int)((ok ? row : 0) % H);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) ss += to_f<T>(ov[e]) * to_f<T>(ov[e]);
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
+    const float r = rsqrtf(ss * (1.f / DV) + eps);
+    const float *wr = wgt + (size_t)h * DV + c0;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e)
+        ov[e] = from_f<T>(to_f<T>(ov[e]) * r * wr[e] / (1.f + __expf(-to_f<T>(gv[e]))));
+    if (ok) *reinterpret_cast<vec *>(o + off) = ov;
+}
+
+// Convolution state of sequences with no tokens: the carried state (or zeros).
+template <typename T>
+__global__ __launch_bounds__(256) void empty_conv_state_kernel(const PrefillParams p, int C)
+{
+    const int s = blockIdx.x / p.H, h = blockIdx.x % p.H;
+    const int slen = p.varlen ? p.cu[s + 1] - p.cu[s] : p.T;
+    if (slen != 0) return;
+    const size_t n = (size_t)(p.f.conv_w - 1) * C, base = ((size_t)s * p.H + h) * n;
+    for (size_t e = threadIdx.x; e < n; e += blockDim.x)
+        ((T *)p.f.conv_state_out)[base + e] = p.f.conv_state ? ((const T *)p.f.conv_state)[base + e] : from_f<T>(0.f);
+}
+
+template <typename T, int DK, int DV, bool ZM, bool PRO>
+static hipError_t launch_intra(const PrefillParams &p, hipStream_t st, unsigned grid)
+{
+    const size_t smem = sizeof(IntraSmem<T, DK, DV>);
+    static const hipError_t attr = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, ZM, PRO>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, ZM, PRO>), dim3(grid), dim3(64 * IWAVES), smem, st, p);
+    return hipSuccess;
+}
+
 template <typename T, int DK, int DV>
 static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
 {
+    static_assert(sizeof(IntraSmem<T, DK, DV>) <= 160 * 1024, "intra-chunk LDS exceeds 160 KiB");
     if (p.varlen)
         hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, p.cu, p.N, p.chunk_off, p.order);
+    const bool pro = p.f.conv_w > 0;
     if (p.n_chunks_cap > 0) {
-        const size_t smem = sizeof(IntraSmem<T, DK, DV>);
-        static_assert(sizeof(IntraSmem<T, DK, DV>) <= 160 * 1024, "intra-chunk LDS exceeds 160 KiB");
-        static const hipError_t attr_z = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, true>,
-                                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        static const hipError_t attr_g = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, false>,
-                                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (attr_z != hipSuccess) return attr_z;
-        if (attr_g != hipSuccess) return attr_g;
         const long items = (long)p.n_chunks_cap * p.H;
         const unsigned grid = (unsigned)(items < intra_grid() ? items : intra_grid());
+        hipError_t e;
         if (p.A_log)
-            hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, true>), dim3(grid), dim3(64 * IWAVES), smem, st, p);
+            e = pro ? launch_intra<T, DK, DV, true, true>(p, st, grid) : launch_intra<T, DK, DV, true, false>(p, st, grid);
         else
-            hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, false>), dim3(grid), dim3(64 * IWAVES), smem, st, p);
+            e = pro ? launch_intra<T, DK, DV, false, true>(p, st, grid) : launch_intra<T, DK, DV, false, false>(p, st, grid);
+        if (e != hipSuccess) return e;
     }
     const long npairs = (long)p.N * p.H;
     const unsigned grid = (unsigned)(((npairs + 7) / 8) * 8 * (DV / 16));
     if (grid > 0) hipLaunchKernelGGL((chain_kernel<T, DK, DV>), dim3(grid), dim3(512), 0, st, p);
+    const long rows = (long)(p.varlen ? p.T : (long)p.N * p.T) * p.H;
+    if (p.f.gate && rows > 0) {
+        constexpr int RPB = 4 * (64 / (DV / (16 / (int)sizeof(T))));  // rows per 256-thread workgroup
+        hipLaunchKernelGGL((gate_norm_kernel<T, DV>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
+                           (T *)p.o, (const T *)p.f.gate, p.f.o_weight, p.H, rows, p.f.o_eps);
+    }
+    if (pro && p.f.conv_state_out && p.f.conv_w > 1 && npairs > 0)
+        hipLaunchKernelGGL(empty_conv_state_kernel<T>, dim3((unsigned)npairs), dim3(256), 0, st, p, 2 * DK + DV);
     return hipGetLastError();
 }
 

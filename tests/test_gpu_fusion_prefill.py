@@ -1,0 +1,196 @@
+"""GPU parity of kda_chunk_fwd with the layer prologue (eq. (2)) and epilogue
+(eq. (6)) fused ("Kimi K3 Technical Report", §2.1.1).
+
+Reference: oracle.layer (fp64).  States and the recurrence output o~ within
+the dtype's bound; convolution states (copies of input values) bit for bit.
+The epilogue divides each (token, head) row by its own RMS, which scales a
+small row's absolute error up with it, so with bf16 operands its output is
+checked in two parts: o~ (the same call without the epilogue) against the
+oracle within the bound, and the fused output against the fp64 epilogue of
+that o~ within EPI_TOL (bf16 output rounding and the fp32 sigmoid / rsqrt).
+Cases span several chunks with a ragged tail, packed sequences shorter than
+the filter, prefix checkpoints, and a prefill handing its states to fused
+decode steps."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.layer as L
+import workloads as W
+from kda_testutil import TOL, np64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+QK_EPS, O_EPS = 1e-6, 1e-6
+EPI_TOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_20_amd as kda
+    kda.load_library()
+
+
+def _wl(dtype=torch.bfloat16, Dk=128, Dv=128, seed=80):
+    return dataclasses.replace(W.WORKLOADS["prefill_8k"], dtype=dtype, Dk=Dk, Dv=Dv, seed=seed)
+
+
+def _plain(d):
+    unit = lambda x: (x.float() / x.float().norm(dim=-1, keepdim=True)).to(x.dtype)
+    return unit(d["q_pre"]), unit(d["k_pre"]), d["v_pre"], torch.sigmoid(d["beta_logit"].float()).to(d["q_pre"].dtype)
+
+
+def _fusion(d, pro, epi, **kw):
+    import gated_delta_rule_20_amd as kda
+    return kda.Fusion(conv_weight=d["conv_weight"] if pro else None, qk_eps=QK_EPS,
+                      gate=d["gate"] if epi else None, o_norm_weight=d["o_norm_weight"] if epi else None,
+                      o_eps=O_EPS, **kw)
+
+
+def _ref(d, pro, epi, cu=None, conv_state=None, h0=None):
+    q, k, v, b = (d["q_pre"], d["k_pre"], d["v_pre"], d["beta_logit"]) if pro else _plain(d)
+    args = [np64(x) for x in (q, k, v, d["z"], b)]
+    if pro:
+        return L.layer_forward(*args, conv_weight=np64(d["conv_weight"]), conv_state=np64(conv_state),
+                               cu_seqlens=cu, h0=np64(h0), A_log=np64(d["A_log"]), g_min=d["g_min"],
+                               qk_eps=QK_EPS, gate=np64(d["gate"]) if epi else None,
+                               o_weight=np64(d["o_norm_weight"]), o_eps=O_EPS)
+    import oracle
+    o, hT = oracle.forward(*args, cu_seqlens=cu, h0=np64(h0), A_log=np64(d["A_log"]), g_min=d["g_min"])
+    if epi:
+        o = L.epilogue(o, np64(d["gate"]), np64(d["o_norm_weight"]), O_EPS)
+    return o, hT, None
+
+
+def _check_output(y, o_plain, d, pro, epi, tol, **ref_kw):
+    """y: the call's output; o_plain: the same call's output without the
+    epilogue.  fp32: y end to end; bf16: o_plain against the oracle and y
+    against the fp64 epilogue of o_plain (see the module docstring)."""
+    if epi and tol > TOL[torch.float32]:
+        o_ref, _, _ = _ref(d, pro, False, **ref_kw)
+        assert rel_err(np64(o_plain), o_ref) <= tol
+        assert rel_err(np64(y), L.epilogue(np64(o_plain), np64(d["gate"]), np64(d["o_norm_weight"]), O_EPS)) <= EPI_TOL
+    else:
+        y_ref, _, _ = _ref(d, pro, epi, **ref_kw)
+        assert rel_err(np64(y), y_ref) <= tol
+
+
+def _prefill(d, pro, epi, q, k, v, b, **kw):
+    """(y, o without the epilogue, final state) of one fused call and, with the
+    epilogue on, a second call without it on the same inputs."""
+    import gated_delta_rule_20_amd as kda
+    fkw = {n: kw.pop(n) for n in ("conv_state", "conv_state_out", "conv_checkpoints") if n in kw}
+    y, hT = kda.chunk_fwd(q, k, v, d["z"], b, A_log=d["A_log"], fusion=_fusion(d, pro, epi, **fkw), **kw)
+    o_plain = y
+    if epi:
+        fkw2 = {n: (torch.empty_like(t) if n != "conv_state" and t is not None else t) for n, t in fkw.items()}
+        kw2 = dict(kw)
+        if kw2.get("checkpoints") is not None:
+            kw2["checkpoints"] = torch.empty_like(kw2["checkpoints"])
+        o_plain, _ = kda.chunk_fwd(q, k, v, d["z"], b, A_log=d["A_log"], fusion=_fusion(d, pro, False, **fkw2), **kw2)
+    torch.cuda.synchronize()
+    return y, o_plain, hT
+
+
+@pytest.mark.parametrize("pro,epi", [(True, True), (True, False), (False, True)])
+@pytest.mark.parametrize("dtype,Dk,Dv,T,cw", [(torch.bfloat16, 128, 128, 200, 4), (torch.bfloat16, 64, 128, 131, 3),
+                                              (torch.bfloat16, 128, 64, 70, 2), (torch.float32, 64, 64, 150, 4)])
+def test_fused_prefill_batched(pro, epi, dtype, Dk, Dv, T, cw):
+    B, H = 2, 3
+    d = W.make_layer(_wl(dtype, Dk, Dv), "cuda", N=B, T=T, H=H, conv_width=cw)
+    q, k, v, b = (d["q_pre"], d["k_pre"], d["v_pre"], d["beta_logit"]) if pro else _plain(d)
+    cs_out = torch.full_like(d["conv_state"], float("nan")) if pro else None
+    y, o_plain, hT = _prefill(d, pro, epi, q, k, v, b, conv_state=d["conv_state"] if pro else None,
+                              conv_state_out=cs_out, initial_state=d["state"])
+    _, h_ref, cs_ref = _ref(d, pro, False, conv_state=d["conv_state"], h0=d["state"])
+    tol = TOL[dtype]
+    _check_output(y, o_plain, d, pro, epi, tol, conv_state=d["conv_state"], h0=d["state"])
+    assert rel_err(np64(hT), h_ref) <= tol
+    if pro:
+        assert np.array_equal(np64(cs_out), cs_ref)
+
+
+@pytest.mark.parametrize("with_state", [True, False])
+def test_fused_prefill_packed_short_sequences(with_state):
+    """Packed sequences of lengths 0..3 (shorter than the filter: the carried
+    state shifts through), around chunk boundaries and longer."""
+    import gated_delta_rule_20_amd as kda
+    lens = [5, 0, 1, 64, 2, 3, 65, 130, 63]
+    N, H = len(lens), 2
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    d = W.make_layer(_wl(seed=81), "cuda", N=1, T=int(cu[-1]), H=H)
+    d2 = W.make_layer(_wl(seed=82), "cuda", N=N, T=1, H=H)     # per-sequence states
+    flat = {n: d[n][0] for n in ("q_pre", "k_pre", "v_pre", "z", "beta_logit", "gate")}
+    flat.update(conv_weight=d["conv_weight"], o_norm_weight=d["o_norm_weight"], A_log=d["A_log"], g_min=d["g_min"])
+    cs_in = d2["conv_state"] if with_state else None
+    cs_out = torch.full_like(d2["conv_state"], float("nan"))
+    cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    y, o_plain, hT = _prefill(flat, True, True, flat["q_pre"], flat["k_pre"], flat["v_pre"], flat["beta_logit"],
+                              conv_state=cs_in, conv_state_out=cs_out, cu_seqlens=cu_t, initial_state=d2["state"])
+    _, h_ref, cs_ref = _ref(flat, True, False, cu=cu, conv_state=cs_in, h0=d2["state"])
+    _check_output(y, o_plain, flat, True, True, TOL[torch.bfloat16], cu=cu, conv_state=cs_in, h0=d2["state"])
+    assert rel_err(np64(hT), h_ref) <= TOL[torch.bfloat16]
+    assert np.array_equal(np64(cs_out), cs_ref)
+
+
+def test_fused_prefill_checkpoints():
+    """State and convolution checkpoints every 64 tokens match the layer run
+    over exactly that prefix; resuming from a pair reproduces the tail."""
+    import gated_delta_rule_20_amd as kda
+    B, H, T, slots = 2, 2, 230, 4
+    d = W.make_layer(_wl(seed=83), "cuda", N=B, T=T, H=H)
+    ck = torch.full((B, slots, H, 128, 128), float("nan"), device="cuda")
+    cck = torch.full((B, slots, H, 3, 384), float("nan"), device="cuda", dtype=torch.bfloat16)
+    f = _fusion(d, True, True, conv_state=d["conv_state"], conv_checkpoints=cck)
+    o, hT = kda.chunk_fwd(d["q_pre"], d["k_pre"], d["v_pre"], d["z"], d["beta_logit"], A_log=d["A_log"],
+                          initial_state=d["state"], checkpoints=ck, checkpoint_every=1, fusion=f)
+    torch.cuda.synchronize()
+    for j in range(slots):
+        P = (j + 1) * 64
+        sub = {n: (d[n][:, :P] if n in ("q_pre", "k_pre", "v_pre", "z", "beta_logit", "gate") else d[n]) for n in d}
+        _, h_ref, cs_ref = _ref(sub, True, True, conv_state=d["conv_state"], h0=d["state"])
+        if P < T:
+            assert rel_err(np64(ck[:, j]), h_ref) <= TOL[torch.bfloat16], j
+            assert np.array_equal(np64(cck[:, j]), cs_ref), j
+        else:
+            assert torch.isnan(ck[:, j]).all() and torch.isnan(cck[:, j].float()).all(), j
+    # resume from slot 1 (position 128) with both states: the tail's o~ and the
+    # final state follow the one-pass run
+    tail = {n: d[n][:, 128:].contiguous() for n in ("q_pre", "k_pre", "v_pre", "z", "beta_logit", "gate")}
+    tail.update({n: d[n] for n in ("conv_weight", "o_norm_weight", "A_log", "g_min")})
+    _, o2, h2 = _prefill(tail, True, True, tail["q_pre"], tail["k_pre"], tail["v_pre"], tail["beta_logit"],
+                         conv_state=cck[:, 1].contiguous(), initial_state=ck[:, 1].contiguous())
+    o_ref, _, _ = _ref(d, True, False, conv_state=d["conv_state"], h0=d["state"])
+    assert rel_err(np64(o2), o_ref[:, 128:]) <= TOL[torch.bfloat16]
+    assert rel_err(np64(h2), np64(hT)) <= TOL[torch.bfloat16]
+
+
+def test_fused_prefill_then_decode():
+    """A fused prefill hands its recurrent and convolution states to fused
+    decode steps; the outputs follow the layer run over the whole stream."""
+    import gated_delta_rule_20_amd as kda
+    N, H, T, K = 3, 2, 100, 3
+    d = W.make_layer(_wl(seed=84), "cuda", N=N, T=T + K, H=H)
+    pre = {n: d[n][:, :T].contiguous() for n in ("q_pre", "k_pre", "v_pre", "z", "beta_logit", "gate")}
+    pre.update({n: d[n] for n in ("conv_weight", "o_norm_weight", "A_log", "g_min")})
+    cs = torch.empty_like(d["conv_state"])
+    y, o_plain, state = _prefill(pre, True, True, pre["q_pre"], pre["k_pre"], pre["v_pre"], pre["beta_logit"],
+                                 conv_state=d["conv_state"], conv_state_out=cs, initial_state=d["state"])
+    ys = []
+    for t in range(T, T + K):
+        sl = lambda n: d[n][:, t].contiguous()
+        f = kda.Fusion(conv_weight=d["conv_weight"], conv_state=cs, qk_eps=QK_EPS, gate=sl("gate"),
+                       o_norm_weight=d["o_norm_weight"], o_eps=O_EPS)
+        ys.append(kda.recurrent_step(sl("q_pre"), sl("k_pre"), sl("v_pre"), sl("z"), sl("beta_logit"), state,
+                                     A_log=d["A_log"], fusion=f))
+    torch.cuda.synchronize()
+    o_ref, h_ref, cs_ref = _ref(d, True, True, conv_state=d["conv_state"], h0=d["state"])
+    _check_output(y, o_plain, pre, True, True, TOL[torch.bfloat16], conv_state=d["conv_state"], h0=d["state"])
+    # the fp32 decode steps end to end
+    assert rel_err(np64(torch.stack(ys, 1)), o_ref[:, T:]) <= TOL[torch.bfloat16]
+    assert rel_err(np64(state), h_ref) <= TOL[torch.bfloat16]
+    assert np.array_equal(np64(cs), cs_ref)
