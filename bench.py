@@ -224,6 +224,80 @@ def bench_spec(T_new=4, calls=None, warmup_rounds=1):
                 N=N, H=H, T_new=T, T_replay=cl[0]["k_r"].shape[1], mean_replayed=n_rep / N, bytes=nbytes)
 
 
+def layer_counts(tokens, N, H, Dk, Dv, W=4, elem=2):
+    """Algorithmic bytes of the fused layer: per (token, head) the projections
+    q, k, v before the convolution, the decay logits z, the beta logit, the gate
+    logits and the output (eq. (2) and eq. (6) inputs and output); per
+    (sequence, head) the fp32 state read and written and the convolution state
+    read and written; the filters once."""
+    per_tok = elem * (3 * Dk + 3 * Dv) + elem
+    per_seq = 2 * Dk * Dv * 4 + 2 * (W - 1) * (2 * Dk + Dv) * elem
+    return per_tok * tokens * H + per_seq * N * H + H * (2 * Dk + Dv) * W * 4 + H * Dv * 4
+
+
+def bench_layer_prefill(steps, warmup, n_sets=3):
+    """prefill_8k shapes through the fused layer (prologue and epilogue in the kernels)."""
+    import dataclasses
+    w = W.WORKLOADS["prefill_8k"]
+    sets = []
+    for i in range(n_sets):
+        d = W.make_layer(dataclasses.replace(w, seed=w.seed + 17 * i), "cuda", N=w.B, T=w.T, H=w.H)
+        f = kda.Fusion(conv_weight=d["conv_weight"], conv_state=d["conv_state"],
+                       conv_state_out=torch.empty_like(d["conv_state"]), qk_eps=1e-6, gate=d["gate"],
+                       o_norm_weight=d["o_norm_weight"], o_eps=1e-6)
+        nws = kda.chunk_fwd_workspace_size(d["q_pre"], d["v_pre"], prologue=True)
+        sets.append((d, f, torch.empty_like(d["v_pre"]), torch.empty_like(d["state"]),
+                     torch.empty(nws, dtype=torch.uint8, device="cuda")))
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        d, f, o, hT, ws = sets[i % n_sets]
+        kda.chunk_fwd(d["q_pre"], d["k_pre"], d["v_pre"], d["z"], d["beta_logit"], A_log=d["A_log"],
+                      g_min=d["g_min"], initial_state=d["state"], out=o, final_state=hT, workspace=ws,
+                      stream=stream, fusion=f)
+
+    for i in range(warmup):
+        call(i)
+    per_call, _ = time_calls(call, steps, stream)
+    B, T, H, Dk = sets[0][0]["q_pre"].shape
+    Dv = sets[0][0]["v_pre"].shape[-1]
+    ms = sum(per_call) / len(per_call)
+    nbytes = layer_counts(B * T, B, H, Dk, Dv)
+    return dict(ms=ms, ms_min=min(per_call), ms_median=statistics.median(per_call), tokens=B * T, bytes=nbytes,
+                shape=(B, T, H, Dk, Dv))
+
+
+def bench_layer_decode(warmup_rounds=1, steps=64):
+    """decode_512 shapes through the fused layer: 64 steps with fresh inputs,
+    the recurrent and convolution states updated in place."""
+    w = W.WORKLOADS["decode_512"]
+    d = W.make_layer(w, "cuda", N=w.B, T=steps, H=w.H)
+    per = [{n: d[n][:, t].contiguous() for n in ("q_pre", "k_pre", "v_pre", "z", "beta_logit", "gate")}
+           for t in range(steps)]
+    for n in ("q_pre", "k_pre", "v_pre", "z", "beta_logit", "gate"):
+        del d[n]
+    state, cs = d["state"], d["conv_state"]
+    fus = [kda.Fusion(conv_weight=d["conv_weight"], conv_state=cs, qk_eps=1e-6, gate=x["gate"],
+                      o_norm_weight=d["o_norm_weight"], o_eps=1e-6) for x in per]
+    outs = [torch.empty_like(x["v_pre"]) for x in per]
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        x = per[i]
+        kda.recurrent_step(x["q_pre"], x["k_pre"], x["v_pre"], x["z"], x["beta_logit"], state, A_log=d["A_log"],
+                           g_min=d["g_min"], out=outs[i], stream=stream, fusion=fus[i])
+
+    for _ in range(warmup_rounds):
+        for i in range(steps):
+            call(i)
+    per_call, _ = time_calls(call, steps, stream)
+    N, H, Dk = per[0]["q_pre"].shape
+    Dv = per[0]["v_pre"].shape[-1]
+    us = 1e3 * sum(per_call) / len(per_call)
+    return dict(us=us, us_min=1e3 * min(per_call), us_median=1e3 * statistics.median(per_call), steps=steps,
+                N=N, H=H, bytes=layer_counts(N, N, H, Dk, Dv))
+
+
 def copy_calibration(steps, nbytes=1 << 30):
     """A plain device-to-device copy of known size (for scaling the HBM
     FETCH_SIZE / WRITE_SIZE counters: it reads and writes nbytes each)."""
@@ -300,7 +374,8 @@ def main():
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured GEMM / copy reference peaks")
     ap.add_argument("--no-spec", action="store_true", help="skip the speculative-decoding replay measurement")
     ap.add_argument("--no-other", action="store_true", help="skip the prefill_128k and varlen_64 measurements")
-    ap.add_argument("--mode", choices=["all", "prefill", "decode", "spec", "copy"], default="all",
+    ap.add_argument("--no-layer", action="store_true", help="skip the fused-layer (prologue / epilogue) measurements")
+    ap.add_argument("--mode", choices=["all", "prefill", "decode", "spec", "layer", "copy"], default="all",
                     help="prefill/decode/copy run one part only (for profiler runs); the JSON line "
                          "of the benchmark contract is printed in mode 'all'")
     args = ap.parse_args()
@@ -321,6 +396,11 @@ def main():
         return
     if args.mode == "spec":
         print(json.dumps(bench_spec()))
+        return
+    if args.mode == "layer":
+        lp = bench_layer_prefill(args.steps, args.warmup)
+        ld = bench_layer_decode()
+        print(json.dumps({"prefill_ms": lp["ms"], "decode_us": ld["us"]}))
         return
 
     pf = bench_prefill(args.steps, args.warmup)
@@ -396,6 +476,32 @@ def main():
                          "algorithmic_bytes": sp["bytes"]},
             "us_per_call_by_new_window": window,
         }
+    if not args.no_layer:
+        lp = bench_layer_prefill(args.steps, args.warmup)
+        ld = bench_layer_decode()
+        lp_gbs = lp["bytes"] / (lp["ms"] / 1e3) / 1e9
+        ld_gbs = ld["bytes"] / (ld["us"] / 1e6) / 1e9
+        B_, T_, H_, Dk_, Dv_ = lp["shape"]
+        result["layer"] = {
+            "what": "eq. (2) prologue (ShortConv width 4, Swish, L2Norm, Sigmoid beta) and eq. (6) epilogue "
+                    "(RMSNorm, Sigmoid output gate) fused around the recurrence; dense projections not included",
+            "prefill": {"workload": f"prefill_8k shapes (B={B_} T={T_} H={H_} d={Dk_}) from pre-convolution "
+                                    "projections, bf16", "ms_per_call": lp["ms"], "ms_median": lp["ms_median"],
+                        "tokens_per_s": lp["tokens"] / (lp["ms"] / 1e3), "vs_core_call": lp["ms"] / pf["ms"],
+                        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd with fusion (intra_chunk_kernel "
+                                     "with prologue + chain_kernel + gate_norm_kernel)", "achieved": lp_gbs,
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lp_gbs / HBM_PEAK_GBS,
+                                     "traffic": profiled_traffic("layer_prefill"), "algorithmic_bytes": lp["bytes"]}},
+            "decode": {"workload": f"decode_512 shapes (N={ld['N']} x 1 token, H={ld['H']}, d=128), fp32 state and "
+                                   f"bf16 convolution state in place, {ld['steps']} steps with fresh inputs",
+                       "us_per_step": ld["us"], "us_median": ld["us_median"],
+                       "tokens_per_s": ld["N"] / (ld["us"] / 1e6),
+                       "roofline": {"bound": "hbm", "kernel": "replay_kernel (fused variant, one-token window)",
+                                    "achieved": ld_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": ld_gbs / HBM_PEAK_GBS, "traffic": profiled_traffic("layer_decode"),
+                                    "algorithmic_bytes": ld["bytes"]}},
+        }
+        torch.cuda.empty_cache()
     if not args.no_other:
         result["other_prefill"] = {
             "prefill_128k: B=1 T=131072 H=32 d=128, 5% of decay channels forced each way": bench_prefill_config("prefill_128k"),

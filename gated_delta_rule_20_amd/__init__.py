@@ -231,13 +231,18 @@ def _chunk_args(q, k, v, g, beta, A_log, g_min, scale, cu_seqlens, N, h0, o, hT,
     return a
 
 
-def chunk_fwd_workspace_size(q, v, *, cu_seqlens=None, N=None) -> int:
+def chunk_fwd_workspace_size(q, v, *, cu_seqlens=None, N=None, prologue: bool = False) -> int:
     """Workspace bytes kda_chunk_fwd needs for q [B,T,H,Dk] (or [T,H,Dk] with
-    cu_seqlens) and v [..., Dv]."""
+    cu_seqlens) and v [..., Dv]; ``prologue``: a fusion with the eq. (2)
+    prologue on (it adds room for the convolved q, k, v, beta)."""
     lib = load_library()
     n = (cu_seqlens.numel() - 1) if cu_seqlens is not None else 0
     a = _chunk_args(q, q, v, q, q, None, -5.0, 1.0, cu_seqlens, N if N is not None else n,
                     None, None, None, None, 0)
+    if prologue:
+        f = LayerFusion()
+        f.conv_width = 1
+        a.fusion = ctypes.pointer(f)
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     out = ctypes.c_size_t(0)
@@ -298,7 +303,8 @@ def chunk_fwd(q, k, v, g, beta, *, A_log=None, g_min: float = -5.0, scale: float
             raise ValueError(f"checkpoints must be [N, slots >= 1, H, Dk, Dv] with N, H, Dk, Dv = "
                              f"{(N, H, Dk, Dv)} and checkpoint_every >= 1; got {tuple(checkpoints.shape)}, "
                              f"every={checkpoint_every}")
-    need = chunk_fwd_workspace_size(q, v, cu_seqlens=cu_seqlens, N=N)
+    need = chunk_fwd_workspace_size(q, v, cu_seqlens=cu_seqlens, N=N,
+                                    prologue=fusion is not None and fusion.prologue)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -213,8 +213,6 @@ template <typename T, int DK, int DV> struct RawIn {
     vu v[HT];
     T beta;
     float alog;
-    ku hk[3], hq[3];   // prologue: pre-activations of the 3 tokens before the segment (oldest first)
-    vu hv[3];
 };
 
 template <typename T, int DK, int DV>
@@ -267,14 +265,23 @@ template <typename V> __device__ __forceinline__ V buf_load(__amdgpu_buffer_rsrc
         return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, 0));
 }
 
-// Where chunk c sits: its first token, token count, sequence, index inside
-// the sequence and the sequence's length.  False if c is past the last chunk
-// (packed tail).
-struct ChunkLoc {
-    int tok0, len, sq, lc, slen;
-};
+// Raw buffer store of a 2-, 4- or 8-byte vector; offsets at or past the
+// descriptor's record count are dropped.
+template <typename V> __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, int voff, V v)
+{
+    if constexpr (sizeof(V) == 2)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), rs, voff, 0, 0);
+    else if constexpr (sizeof(V) == 4)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff, 0, 0);
+    else
+    {
+        typedef unsigned u32x2 __attribute__((vector_size(8)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, voff, 0, 0);
+    }
+}
 
-__device__ __forceinline__ bool locate_chunk(const PrefillParams &p, int c, ChunkLoc &cl)
+// Token range of chunk c; false if c is past the last chunk (packed tail).
+__device__ __forceinline__ bool locate_chunk(const PrefillParams &p, int c, int &tok0, int &len)
 {
     if (p.varlen) {
         if (c >= ld_uniform(p.chunk_off, p.N)) return false;
@@ -283,114 +290,61 @@ __device__ __forceinline__ bool locate_chunk(const PrefillParams &p, int c, Chun
             const int mid = (lo + hi + 1) >> 1;
             if (ld_uniform(p.chunk_off, mid) <= c) lo = mid; else hi = mid - 1;
         }
-        const int start = ld_uniform(p.cu, lo);
-        cl.sq = lo;
-        cl.lc = c - ld_uniform(p.chunk_off, lo);
-        cl.slen = ld_uniform(p.cu, lo + 1) - start;
-        cl.tok0 = start + cl.lc * CHUNK;
-        cl.len = min(CHUNK, cl.slen - cl.lc * CHUNK);
+        tok0 = ld_uniform(p.cu, lo) + (c - ld_uniform(p.chunk_off, lo)) * CHUNK;
+        len = min(CHUNK, ld_uniform(p.cu, lo + 1) - tok0);
     } else {
         const int cps = (p.T + CHUNK - 1) / CHUNK;
-        cl.sq = c / cps;
-        cl.lc = c - cl.sq * cps;
-        cl.slen = p.T;
-        cl.tok0 = cl.sq * p.T + cl.lc * CHUNK;
-        cl.len = min(CHUNK, p.T - cl.lc * CHUNK);
+        const int s = c / cps, lc = c - s * cps;
+        tok0 = s * p.T + lc * CHUNK;
+        len = min(CHUNK, p.T - lc * CHUNK);
     }
+    return true;
+}
+
+// Sequence of chunk c, its index inside the sequence and the sequence's length
+// (besides the token range); false if c is past the last chunk.
+__device__ __forceinline__ bool locate_seq(const PrefillParams &p, int c, int &tok0, int &len, int &sq, int &lc,
+                                           int &slen)
+{
+    if (p.varlen) {
+        if (c >= ld_uniform(p.chunk_off, p.N)) return false;
+        int lo = 0, hi = p.N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (ld_uniform(p.chunk_off, mid) <= c) lo = mid; else hi = mid - 1;
+        }
+        const int start = ld_uniform(p.cu, lo);
+        sq = lo;
+        lc = c - ld_uniform(p.chunk_off, lo);
+        slen = ld_uniform(p.cu, lo + 1) - start;
+    } else {
+        const int cps = (p.T + CHUNK - 1) / CHUNK;
+        sq = c / cps;
+        lc = c - sq * cps;
+        slen = p.T;
+    }
+    tok0 = (p.varlen ? ld_uniform(p.cu, sq) : sq * p.T) + lc * CHUNK;
+    len = min(CHUNK, slen - lc * CHUNK);
     return true;
 }
 
 // Next valid item at or after i (stride gridDim.x); items run chunk-major
 // from the last chunk down.  Returns false when the walk is done.
-__device__ __forceinline__ bool next_item(const PrefillParams &p, int &i, int &c, int &h, ChunkLoc &cl)
+__device__ __forceinline__ bool next_item(const PrefillParams &p, int &i, int &c, int &h, int &tok0, int &len)
 {
     const int n_items = p.n_chunks_cap * p.H;
     for (; i < n_items; i += gridDim.x) {
         const int ci = i / p.H;
         h = i - ci * p.H;
         c = p.n_chunks_cap - 1 - ci;
-        if (locate_chunk(p, c, cl)) return true;
+        if (locate_chunk(p, c, tok0, len)) return true;
     }
     return false;
 }
 
-// Prologue: the pre-activations of the 3 tokens before the wave's segment
-// (token tb of item cl, head h), oldest first, into in.hq / hk / hv.  They
-// come from the token arrays when they lie in the sequence, from conv_state
-// (row j = slot - 4 + W) at a sequence start, and are zero past the filter,
-// without conv_state, or for a segment past the chunk's end.
-template <typename T, int DK, int DV>
-__device__ __forceinline__ void load_hist(RawIn<T, DK, DV> &in, const PrefillParams &p, const ChunkLoc &cl, bool have,
-                                          int h, int tb, int l)
-{
-    using R = RawIn<T, DK, DV>;
-    typedef typename R::ku ku;
-    typedef typename R::vu vu;
-    constexpr int EL = (int)sizeof(T), C = 2 * DK + DV;
-    const int rowk = p.H * DK * EL, rowv = p.H * DV * EL;
-    const bool seg = have && tb < cl.len;
-    const bool from_state = tb == 0 && cl.lc == 0;
-    if (from_state) {
-        const bool st = seg && p.f.conv_state && p.f.conv_w > 1;
-        const int W = p.f.conv_w;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)((const T *)(st ? p.f.conv_state : p.q) + (st ? ((size_t)cl.sq * p.H + h) * (W - 1) * C : 0)), 0,
-            st ? (W - 1) * C * EL : 0, 0x00020000);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            const int j = i - 4 + W;
-            const int ro = j >= 0 ? j * C * EL : 0x40000000;  // past the record count: reads as zero
-            in.hq[i] = buf_load<ku>(rs, ro + R::CPT * l * EL);
-            in.hk[i] = buf_load<ku>(rs, ro + (DK + R::CPT * l) * EL);
-            in.hv[i] = buf_load<vu>(rs, ro + (2 * DK + R::CPV * l) * EL);
-        }
-    } else {
-        // tokens tb - 3 .. tb - 1 of the same sequence (the previous chunk's tail when tb = 0)
-        const size_t row0 = seg ? (size_t)(cl.tok0 + tb - 3) * p.H + h : 0;
-        const int reck = seg ? 2 * rowk + DK * EL : 0, recv = seg ? 2 * rowv + DV * EL : 0;
-        const __amdgpu_buffer_rsrc_t rsq = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.q + row0 * DK), 0, reck, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.k + row0 * DK), 0, reck, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.v + row0 * DV), 0, recv, 0x00020000);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            in.hq[i] = buf_load<ku>(rsq, i * rowk + R::CPT * l * EL);
-            in.hk[i] = buf_load<ku>(rsk, i * rowk + R::CPT * l * EL);
-            in.hv[i] = buf_load<vu>(rsv, i * rowv + R::CPV * l * EL);
-        }
-    }
-}
-
-// Sums each of 16 per-lane values over the wave's 64 lanes (a transposed
-// butterfly: each exchange halves the values a lane carries, 17 lane swaps in
-// all instead of 96) and returns total i, uniform, in out[i].
-__device__ __forceinline__ void wave_sum16(const float (&v)[16], float (&out)[16], int l)
-{
-    float a[8], b[4], c[2];
-    const bool b5 = l & 32, b4 = l & 16, b3 = l & 8, b2 = l & 4;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = (b5 ? v[i + 8] : v[i]) + __shfl_xor(b5 ? v[i] : v[i + 8], 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = (b4 ? a[i + 4] : a[i]) + __shfl_xor(b4 ? a[i] : a[i + 4], 16);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) c[i] = (b3 ? b[i + 2] : b[i]) + __shfl_xor(b3 ? b[i] : b[i + 2], 8);
-    float d = (b2 ? c[1] : c[0]) + __shfl_xor(b2 ? c[0] : c[1], 4);  // value 8 b5 + 4 b4 + 2 b3 + b2
-    d += __shfl_xor(d, 2);
-    d += __shfl_xor(d, 1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) out[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d), 4 * i));
-}
-
 // ZM: decay logits z with the eq. (5) gate (A_log given), else log-decays g;
 // a template parameter so the elementwise pass carries no per-element branch.
-//
-// PRO: the layer's input prologue (eq. (2)) runs first in P1: each wave
-// convolves its 8 tokens with the 3 pre-activations before them (ShortConv,
-// taps zero-padded to width 4), applies Swish, zeroes tokens past the chunk
-// (the convolution would otherwise give them values), L2-normalises q and k
-// with one 16-value wave reduction, and applies Sigmoid to the beta logits.
-// The last chunk of a sequence writes its convolution state, checkpoint
-// chunks their convolution checkpoints.
-template <typename T, int DK, int DV, bool ZM, bool PRO>
+template <typename T, int DK, int DV, bool ZM>
 __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 {
     using BL = Block<T, DK, DV>;
@@ -407,16 +361,13 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
     const int ch0 = CPT * l;  // first channel of this lane in the elementwise phase
     const int m0 = w & 3, hf = w >> 2, tb = seg_base(w);  // elementwise: tile, half, first token
 
-    int i = blockIdx.x, c, h;
-    ChunkLoc cl{};
-    bool have = next_item(p, i, c, h, cl);
+    int i = blockIdx.x, c, h, tok0, len;
+    bool have = next_item(p, i, c, h, tok0, len);
     R raw;
-    if (have) load_raw(raw, p, cl.tok0, cl.len, h, w, l);
-    if constexpr (PRO) load_hist(raw, p, cl, have, h, tb, l);
+    if (have) load_raw(raw, p, tok0, len, h, w, l);
     __builtin_amdgcn_s_waitcnt(0);
 
     while (have) {
-        const int tok0 = cl.tok0, len = cl.len;
         char *blkb = p.blocks + ((size_t)h * p.n_chunks_cap + c) * BL::BYTES;
         T *blk = reinterpret_cast<T *>(blkb);
         float *gamma_out = reinterpret_cast<float *>(blkb + BL::GAMMA_BYTE);
@@ -427,10 +378,8 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         // wait here holds back on the previous item's result stores.
         // The next item's raw inputs are loaded into each raw register right after
         // its last use below, so the loads issue between this item's VALU work.
-        int i2 = i + gridDim.x, c2 = 0, h2 = 0;
-        ChunkLoc cl2{};
-        const bool have2 = next_item(p, i2, c2, h2, cl2);
-        const int tok2 = cl2.tok0, len2 = cl2.len;
+        int i2 = i + gridDim.x, c2 = 0, h2 = 0, tok2 = 0, len2 = 0;
+        const bool have2 = next_item(p, i2, c2, h2, tok2, len2);
         // The next item's rows of this wave through buffer descriptors: base at its
         // first token (uniform), lane offset plus token offset in one VGPR shared by
         // g, k and q, and a record count that ends at the last valid token, so tokens
@@ -445,99 +394,6 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         const __amdgpu_buffer_rsrc_t rsq = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.q + row0 * DK), 0, reck, 0x00020000);
         const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.v + row0 * DV), 0, recv, 0x00020000);
         const int offk = ch0 * (int)sizeof(T), offv = CPV * l * (int)sizeof(T);
-        // ---- P1 prologue (eq. (2)): q, k, v activations of the wave's tokens ----
-        float ka[PRO ? HT : 1][CPT], qa[PRO ? HT : 1][CPT], va[PRO ? HT : 1][CPV];
-        if constexpr (PRO) {
-            constexpr int C = 2 * DK + DV;
-            const int W = p.f.conv_w;
-            float wq[CPT][4], wk[CPT][4], wv[CPV][4];  // taps, newest last, zero-padded at the old end
-            const float *wb = p.f.conv_weight + (size_t)h * C * W;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int xw = e - 4 + W;
-#pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) {
-                    wq[cc][e] = xw >= 0 ? wb[(ch0 + cc) * W + xw] : 0.f;
-                    wk[cc][e] = xw >= 0 ? wb[(DK + ch0 + cc) * W + xw] : 0.f;
-                }
-#pragma unroll
-                for (int cv = 0; cv < CPV; ++cv) wv[cv][e] = xw >= 0 ? wb[(2 * DK + CPV * l + cv) * W + xw] : 0.f;
-            }
-            auto swish = [](float u) { return u * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-LOG2E * u)); };
-            float ssq[16];  // per token: sum of a_k^2 (0..7), a_q^2 (8..15) over this lane's channels
-#pragma unroll
-            for (int r0 = 0; r0 < HT; ++r0) {
-                const bool ok = tb + r0 < len;
-                ssq[r0] = 0.f;
-                ssq[HT + r0] = 0.f;
-#pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) {
-                    float cq = 0.f, ck = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {  // token r0 - 3 + e; negative: history slot
-                        const int rr = r0 - 3 + e;
-                        cq += wq[cc][e] * to_f<T>(rr < 0 ? raw.hq[rr + 3][cc] : raw.q[rr < 0 ? 0 : rr][cc]);
-                        ck += wk[cc][e] * to_f<T>(rr < 0 ? raw.hk[rr + 3][cc] : raw.k[rr < 0 ? 0 : rr][cc]);
-                    }
-                    qa[r0][cc] = ok ? swish(cq) : 0.f;
-                    ka[r0][cc] = ok ? swish(ck) : 0.f;
-                    ssq[r0] += ka[r0][cc] * ka[r0][cc];
-                    ssq[HT + r0] += qa[r0][cc] * qa[r0][cc];
-                }
-#pragma unroll
-                for (int cv = 0; cv < CPV; ++cv) {
-                    float cx = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int rr = r0 - 3 + e;
-                        cx += wv[cv][e] * to_f<T>(rr < 0 ? raw.hv[rr + 3][cv] : raw.v[rr < 0 ? 0 : rr][cv]);
-                    }
-                    va[r0][cv] = ok ? swish(cx) : 0.f;
-                }
-            }
-            float tot[16];
-            wave_sum16(ssq, tot, l);
-#pragma unroll
-            for (int r0 = 0; r0 < HT; ++r0) {
-                const float nk = rsqrtf(tot[r0] + p.f.qk_eps), nq = rsqrtf(tot[HT + r0] + p.f.qk_eps);
-#pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) {
-                    ka[r0][cc] *= nk;
-                    qa[r0][cc] *= nq;
-                }
-            }
-            // Convolution state after the sequence (last chunk) and at checkpoint
-            // positions: the pre-activations of chunk positions q0 .. q0 + W - 2; a
-            // position before the chunk (q < 0) is history slot q + 3 of wave tb = 0.
-            auto put_rows = [&](T *dst, int q0) {
-                for (int j = 0; j < W - 1; ++j) {
-                    const int qp = q0 + j;
-                    const bool mine = (qp < 0) ? (tb == 0) : (qp >= tb && qp < tb + HT);
-                    if (!mine) continue;
-                    const int sl = qp < 0 ? qp + 3 : 0, rr = qp < 0 ? 0 : qp - tb;
-                    ku xq = raw.q[0], xk = raw.k[0];
-                    typename R::vu xv = raw.v[0];
-#pragma unroll
-                    for (int e = 0; e < HT; ++e)
-                        if (qp >= 0 && rr == e) { xq = raw.q[e]; xk = raw.k[e]; xv = raw.v[e]; }
-#pragma unroll
-                    for (int e = 0; e < 3; ++e)
-                        if (qp < 0 && sl == e) { xq = raw.hq[e]; xk = raw.hk[e]; xv = raw.hv[e]; }
-                    *reinterpret_cast<ku *>(dst + j * C + ch0) = xq;
-                    *reinterpret_cast<ku *>(dst + j * C + DK + ch0) = xk;
-                    *reinterpret_cast<typename R::vu *>(dst + j * C + 2 * DK + CPV * l) = xv;
-                }
-            };
-            if (p.f.conv_state_out && cl.lc * CHUNK + len == cl.slen)
-                put_rows((T *)p.f.conv_state_out + ((size_t)cl.sq * p.H + h) * (W - 1) * C, len - (W - 1));
-            if (p.f.conv_ckpt && p.ckpt_every > 0 && (cl.lc + 1) % p.ckpt_every == 0) {
-                const int slot = (cl.lc + 1) / p.ckpt_every - 1;
-                if (slot < p.ckpt_slots && (cl.lc + 1) * CHUNK < cl.slen)
-                    put_rows((T *)p.f.conv_ckpt + (((size_t)cl.sq * p.ckpt_slots + slot) * p.H + h) * (W - 1) * C,
-                             CHUNK - (W - 1));
-            }
-            load_hist(raw, p, cl2, have2, h2, tb, l);  // the next item's history (registers now free)
-        }
         float lam2[HT][CPT];  // (lam_r - B_m) log2(e) for this wave's tokens (tile m = w % 4)
         {
             const float cz = -__expf(raw.alog) * LOG2E;  // exp(-e^A z) = exp2(cz z)
@@ -559,10 +415,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             }
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) sm.tot[2 * m0 + hf][ch0 + cc] = run[cc];
-            if (l < HT) {
-                const float b = to_f<T>(raw.beta);  // PRO: the logit W_beta x
-                sm.beta[tb + l] = PRO ? (tb + l < len ? 1.f / (1.f + __expf(-b)) : 0.f) : b;
-            }
+            if (l < HT) sm.beta[tb + l] = to_f<T>(raw.beta);
         }
         {
             const int bt = tb + l;
@@ -602,8 +455,8 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 ku kr_, qr_, kc_, ke_, kx1_, kx2_;
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) {
-                    const float kv = PRO ? ka[PRO ? r0 : 0][cc] : to_f<T>(raw.k[r0][cc]);
-                    const float qv = p.scale * (PRO ? qa[PRO ? r0 : 0][cc] : to_f<T>(raw.q[r0][cc]));
+                    const float kv = to_f<T>(raw.k[r0][cc]);
+                    const float qv = p.scale * to_f<T>(raw.q[r0][cc]);
                     const float eR = __builtin_amdgcn_exp2f(lam2[r0][cc]);        // exp(lam_r - B_w) <= 1
                     const float eC = __builtin_amdgcn_rcpf(eR);  // exp(B_w - lam_r) <= e^80
                     const float kr = kv * eR, qr = qv * eR, kcs = kv * eC, kce = kcs * eT[cc];
@@ -643,7 +496,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             for (int cv = 0; cv < CPV; ++cv) {
                 tok8 col;
 #pragma unroll
-                for (int r = 0; r < HT; ++r) col[r] = PRO ? from_f<T>(va[PRO ? r : 0][cv]) : raw.v[r][cv];
+                for (int r = 0; r < HT; ++r) col[r] = raw.v[r][cv];
                 *reinterpret_cast<tok8 *>(&sm.VT[CPV * l + cv][tb]) = col;
             }
 #pragma unroll
@@ -830,7 +683,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             }
         }
         lds_barrier();  // LDS is reused by the next item
-        i = i2; c = c2; h = h2; cl = cl2;
+        i = i2; c = c2; h = h2; tok0 = tok2; len = len2;
         have = have2;
     }
 }
@@ -1085,18 +938,203 @@ __global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
 }
 
 // -----------------------------------------------------------------------------
-// Persistent grid of the intra-chunk stage: one workgroup per compute unit
-// (its LDS footprint allows one), queried once from the device.
-static long intra_grid()
+// Layer prologue (eq. (2)) as a pass of its own ahead of the intra-chunk stage.
+// (Folded into the intra-chunk kernel's elementwise phase it pushed that kernel
+// past its register budget: spills on the prefetched inputs serialised their
+// loads and tripled its time.)  One workgroup per (chunk, head); wave w takes
+// tokens 16 w .. 16 w + 15 of the chunk, lane l the query and key channels
+// CPT*l.. and the value channels CPV*l.., and reads 19 rows of each projection
+// (the 16 tokens and the 3 before them: the previous chunk of the same
+// sequence, or conv_state at a sequence start).  Per token and channel:
+// ShortConv (taps zero-padded to width 4), Swish, and for q and k L2Norm over
+// the head's channels (one 16-value wave reduction per 8 tokens: their 8 key
+// and 8 query norms); Sigmoid of the beta logit.  bf16 q, k, v, beta go to the workspace, where the intra-chunk stage
+// reads them in place of its inputs.  The last chunk of a sequence also writes
+// the convolution state, a checkpoint chunk its convolution checkpoint.
+
+// Sums each of 16 per-lane values over the wave's 64 lanes (a transposed
+// butterfly: each exchange halves the values a lane carries, 17 lane swaps in
+// all instead of 96); every lane receives the 16 totals.
+__device__ __forceinline__ void wave_sum16(const float (&v)[16], float (&out)[16], int l)
 {
-    static const long n = [] {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-        return (long)cus;
-    }();
-    return n;
+    float a[8], b[4], c[2];
+    const bool b5 = l & 32, b4 = l & 16, b3 = l & 8, b2 = l & 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (b5 ? v[i + 8] : v[i]) + __shfl_xor(b5 ? v[i] : v[i + 8], 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = (b4 ? a[i + 4] : a[i]) + __shfl_xor(b4 ? a[i] : a[i + 4], 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) c[i] = (b3 ? b[i + 2] : b[i]) + __shfl_xor(b3 ? b[i] : b[i + 2], 8);
+    float d = (b2 ? c[1] : c[0]) + __shfl_xor(b2 ? c[0] : c[1], 4);  // value 8 b5 + 4 b4 + 2 b3 + b2
+    d += __shfl_xor(d, 2);
+    d += __shfl_xor(d, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = __shfl(d, 4 * i);
+}
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void prologue_kernel(PrefillParams p)
+{
+    constexpr int C = 2 * DK + DV, CPT = DK / 64, CPV = DV / 64, TW = 16, NR = TW + 3, HW = 8;
+    constexpr int EL = (int)sizeof(T);
+    typedef typename Vec<T, CPT>::type ku;
+    typedef typename Vec<T, CPV>::type vu;
+    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = blockIdx.x, h = blockIdx.y;
+    int tok0, len, sq, lc, slen;
+    if (!locate_seq(p, c, tok0, len, sq, lc, slen)) return;
+    const int tb = TW * w;
+    if (tb >= len) return;
+    const int W = p.f.conv_w;
+    const int rowk = p.H * DK * EL, rowv = p.H * DV * EL;
+
+    // rows 0..2: positions tb - 3 .. tb - 1; rows 3..18: the wave's tokens (zero past the chunk)
+    ku xq[NR], xk[NR];
+    vu xv[NR];
+    {
+        // All 19 rows are requested before any is used: the 3 history rows through
+        // one descriptor over either the 3 tokens before (same sequence) or this
+        // sequence's conv_state rows (slot i = row i - 4 + W; older slots, or no
+        // conv_state, read past the record count and give zeros).
+        const bool tok_hist = tb > 0 || lc > 0;
+        const T *cs = (const T *)p.f.conv_state;
+        const bool st = !tok_hist && cs && W > 1;
+        const size_t rh = tok_hist ? (size_t)(tok0 + tb - 3) * p.H + h : 0;
+        const __amdgpu_buffer_rsrc_t hq = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(st ? cs + ((size_t)sq * p.H + h) * (W - 1) * C : (const T *)p.q + rh * DK), 0,
+            st ? (W - 1) * C * EL : (tok_hist ? 2 * rowk + DK * EL : 0), 0x00020000);
+        const __amdgpu_buffer_rsrc_t hk = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(st ? cs + ((size_t)sq * p.H + h) * (W - 1) * C + DK : (const T *)p.k + rh * DK), 0,
+            st ? (W - 1) * C * EL - DK * EL : (tok_hist ? 2 * rowk + DK * EL : 0), 0x00020000);
+        const __amdgpu_buffer_rsrc_t hv = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(st ? cs + ((size_t)sq * p.H + h) * (W - 1) * C + 2 * DK : (const T *)p.v + rh * DV), 0,
+            st ? (W - 1) * C * EL - 2 * DK * EL : (tok_hist ? 2 * rowv + DV * EL : 0), 0x00020000);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int j = i - 4 + W;
+            const int sk = st ? (j >= 0 ? j * C * EL : 0x40000000) : i * rowk;  // row offset, per descriptor
+            const int sv = st ? (j >= 0 ? j * C * EL : 0x40000000) : i * rowv;
+            xq[i] = buf_load<ku>(hq, sk + CPT * l * EL);
+            xk[i] = buf_load<ku>(hk, sk + CPT * l * EL);
+            xv[i] = buf_load<vu>(hv, sv + CPV * l * EL);
+        }
+        const int nv = min(len - tb, TW);
+        const size_t r0 = (size_t)(tok0 + tb) * p.H + h;
+        const int rk = (nv - 1) * rowk + DK * EL, rv = (nv - 1) * rowv + DV * EL;
+        const __amdgpu_buffer_rsrc_t dq = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.q + r0 * DK), 0, rk, 0x00020000);
+        const __amdgpu_buffer_rsrc_t dk = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.k + r0 * DK), 0, rk, 0x00020000);
+        const __amdgpu_buffer_rsrc_t dv = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.v + r0 * DV), 0, rv, 0x00020000);
+#pragma unroll
+        for (int r = 0; r < TW; ++r) {
+            xq[3 + r] = buf_load<ku>(dq, r * rowk + CPT * l * EL);
+            xk[3 + r] = buf_load<ku>(dk, r * rowk + CPT * l * EL);
+            xv[3 + r] = buf_load<vu>(dv, r * rowv + CPV * l * EL);
+        }
+    }
+    const float *wb = p.f.conv_weight + (size_t)h * C * W;
+    auto taps = [&](int chan, float (&t4)[4]) {  // newest last, zero-padded at the old end
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int xw = e - 4 + W;
+            t4[e] = xw >= 0 ? wb[chan * W + xw] : 0.f;
+        }
+    };
+    auto swish = [](float u) { return u * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-LOG2E * u)); };
+
+    // Outputs through descriptors whose record count ends at the chunk's last
+    // token: stores past it are dropped, so no per-token branch is needed.
+    const int nv = min(len - tb, TW);
+    const size_t r0 = (size_t)(tok0 + tb) * p.H + h;
+    const int rk = (nv - 1) * rowk + DK * EL, rv = (nv - 1) * rowv + DV * EL;
+    const __amdgpu_buffer_rsrc_t oq = __builtin_amdgcn_make_buffer_rsrc((void *)((T *)p.pro_q + r0 * DK), 0, rk, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ok_ = __builtin_amdgcn_make_buffer_rsrc((void *)((T *)p.pro_k + r0 * DK), 0, rk, 0x00020000);
+    // q and k, in two halves of 8 tokens: convolve, Swish, then L2Norm with the
+    // half's 8 key and 8 query sums of squares in one 16-value reduction
+    float tq[CPT][4], tk[CPT][4];
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+        taps(CPT * l + cc, tq[cc]);
+        taps(DK + CPT * l + cc, tk[cc]);
+    }
+#pragma unroll
+    for (int hb = 0; hb < TW; hb += HW) {
+        float a[2][HW][CPT], ss[2 * HW];
+#pragma unroll
+        for (int sidx = 0; sidx < 2; ++sidx) {  // 0: keys, 1: queries
+#pragma unroll
+            for (int r = 0; r < HW; ++r) {
+                ss[sidx * HW + r] = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    float cx = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        cx += (sidx ? tq : tk)[cc][e] * to_f<T>((sidx ? xq[hb + r + e] : xk[hb + r + e])[cc]);
+                    a[sidx][r][cc] = swish(cx);
+                    ss[sidx * HW + r] += a[sidx][r][cc] * a[sidx][r][cc];
+                }
+            }
+        }
+        float tot[2 * HW];
+        wave_sum16(ss, tot, l);
+#pragma unroll
+        for (int sidx = 0; sidx < 2; ++sidx) {
+#pragma unroll
+            for (int r = 0; r < HW; ++r) {
+                const float n = rsqrtf(tot[sidx * HW + r] + p.f.qk_eps);
+                ku o;
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) o[cc] = from_f<T>(a[sidx][r][cc] * n);
+                buf_store<ku>(sidx ? oq : ok_, (hb + r) * rowk + CPT * l * EL, o);
+            }
+        }
+    }
+    {   // v: convolve, Swish, store
+        float t4[CPV][4];
+#pragma unroll
+        for (int cv = 0; cv < CPV; ++cv) taps(2 * DK + CPV * l + cv, t4[cv]);
+        const __amdgpu_buffer_rsrc_t od = __builtin_amdgcn_make_buffer_rsrc((void *)((T *)p.pro_v + r0 * DV), 0, rv, 0x00020000);
+#pragma unroll
+        for (int r = 0; r < TW; ++r) {
+            vu o;
+#pragma unroll
+            for (int cv = 0; cv < CPV; ++cv) {
+                float cx = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cx += t4[cv][e] * to_f<T>(xv[r + e][cv]);
+                o[cv] = from_f<T>(swish(cx));
+            }
+            buf_store<vu>(od, r * rowv + CPV * l * EL, o);
+        }
+    }
+    {   // beta = Sigmoid(logit), lanes 0..15
+        const int rb = (nv - 1) * p.H * EL + EL;
+        const __amdgpu_buffer_rsrc_t ib = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.beta + r0), 0, rb, 0x00020000);
+        const __amdgpu_buffer_rsrc_t ob = __builtin_amdgcn_make_buffer_rsrc((void *)((T *)p.pro_b + r0), 0, rb, 0x00020000);
+        const int off = (l < TW ? l : 0x4000000) * p.H * EL;  // lanes past the wave's tokens read and write nothing
+        const T b = buf_load<T>(ib, off);
+        buf_store<T>(ob, off, from_f<T>(1.f / (1.f + __expf(-to_f<T>(b)))));
+    }
+    // Convolution state: the pre-activations of chunk positions q0 .. q0 + W - 2,
+    // taken by the wave whose rows hold them (position q is row q - tb + 3).
+    auto put_rows = [&](T *dst, int q0) {
+#pragma unroll
+        for (int e = 0; e < NR; ++e) {  // row e holds chunk position tb - 3 + e
+            const int j = tb - 3 + e - q0;  // its state row
+            if (j < 0 || j >= W - 1 || (e < 3 && tb - 3 + e >= 0)) continue;  // not kept, or another wave's token
+            *reinterpret_cast<ku *>(dst + (size_t)j * C + CPT * l) = xq[e];
+            *reinterpret_cast<ku *>(dst + (size_t)j * C + DK + CPT * l) = xk[e];
+            *reinterpret_cast<vu *>(dst + (size_t)j * C + 2 * DK + CPV * l) = xv[e];
+        }
+    };
+    if (W > 1 && p.f.conv_state_out && lc * CHUNK + len == slen)
+        put_rows((T *)p.f.conv_state_out + ((size_t)sq * p.H + h) * (W - 1) * C, len - (W - 1));
+    if (W > 1 && p.f.conv_ckpt && p.ckpt_every > 0 && (lc + 1) % p.ckpt_every == 0) {
+        const int slot = (lc + 1) / p.ckpt_every - 1;
+        if (slot < p.ckpt_slots && (lc + 1) * CHUNK < slen)
+            put_rows((T *)p.f.conv_ckpt + (((size_t)sq * p.ckpt_slots + slot) * p.H + h) * (W - 1) * C,
+                     CHUNK - (W - 1));
+    }
 }
 
 // -----------------------------------------------------------------------------
@@ -1144,33 +1182,48 @@ __global__ __launch_bounds__(256) void empty_conv_state_kernel(const PrefillPara
         ((T *)p.f.conv_state_out)[base + e] = p.f.conv_state ? ((const T *)p.f.conv_state)[base + e] : from_f<T>(0.f);
 }
 
-template <typename T, int DK, int DV, bool ZM, bool PRO>
-static hipError_t launch_intra(const PrefillParams &p, hipStream_t st, unsigned grid)
+// -----------------------------------------------------------------------------
+// Persistent grid of the intra-chunk stage: one workgroup per compute unit
+// (its LDS footprint allows one), queried once from the device.
+static long intra_grid()
 {
-    const size_t smem = sizeof(IntraSmem<T, DK, DV>);
-    static const hipError_t attr = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, ZM, PRO>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, ZM, PRO>), dim3(grid), dim3(64 * IWAVES), smem, st, p);
-    return hipSuccess;
+    static const long n = [] {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        return (long)cus;
+    }();
+    return n;
 }
 
 template <typename T, int DK, int DV>
 static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
 {
-    static_assert(sizeof(IntraSmem<T, DK, DV>) <= 160 * 1024, "intra-chunk LDS exceeds 160 KiB");
     if (p.varlen)
         hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, p.cu, p.N, p.chunk_off, p.order);
     const bool pro = p.f.conv_w > 0;
+    if (pro && p.n_chunks_cap > 0)
+        hipLaunchKernelGGL((prologue_kernel<T, DK, DV>), dim3((unsigned)p.n_chunks_cap, (unsigned)p.H), dim3(256), 0, st, p);
+    PrefillParams pi = p;  // with the prologue, the intra-chunk stage reads its outputs
+    if (pro) {
+        pi.q = p.pro_q; pi.k = p.pro_k; pi.v = p.pro_v; pi.beta = p.pro_b;
+    }
     if (p.n_chunks_cap > 0) {
+        const size_t smem = sizeof(IntraSmem<T, DK, DV>);
+        static_assert(sizeof(IntraSmem<T, DK, DV>) <= 160 * 1024, "intra-chunk LDS exceeds 160 KiB");
+        static const hipError_t attr_z = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, true>,
+                                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        static const hipError_t attr_g = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, false>,
+                                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (attr_z != hipSuccess) return attr_z;
+        if (attr_g != hipSuccess) return attr_g;
         const long items = (long)p.n_chunks_cap * p.H;
         const unsigned grid = (unsigned)(items < intra_grid() ? items : intra_grid());
-        hipError_t e;
         if (p.A_log)
-            e = pro ? launch_intra<T, DK, DV, true, true>(p, st, grid) : launch_intra<T, DK, DV, true, false>(p, st, grid);
+            hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, true>), dim3(grid), dim3(64 * IWAVES), smem, st, pi);
         else
-            e = pro ? launch_intra<T, DK, DV, false, true>(p, st, grid) : launch_intra<T, DK, DV, false, false>(p, st, grid);
-        if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, false>), dim3(grid), dim3(64 * IWAVES), smem, st, pi);
     }
     const long npairs = (long)p.N * p.H;
     const unsigned grid = (unsigned)(((npairs + 7) / 8) * 8 * (DV / 16));
@@ -1181,7 +1234,8 @@ static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
         hipLaunchKernelGGL((gate_norm_kernel<T, DV>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
                            (T *)p.o, (const T *)p.f.gate, p.f.o_weight, p.H, rows, p.f.o_eps);
     }
-    if (pro && p.f.conv_state_out && p.f.conv_w > 1 && npairs > 0)
+    // sequences without tokens (packed, or T = 0) get the carried convolution state
+    if (pro && p.f.conv_state_out && p.f.conv_w > 1 && npairs > 0 && (p.varlen || p.T == 0))
         hipLaunchKernelGGL(empty_conv_state_kernel<T>, dim3((unsigned)npairs), dim3(256), 0, st, p, 2 * DK + DV);
     return hipGetLastError();
 }

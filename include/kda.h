@@ -182,8 +182,10 @@ typedef struct {
     const kda_layer_fusion_t *fusion;   /* optional prologue / epilogue, or NULL */
 } kda_chunk_fwd_args_t;
 
-/* Workspace bytes kda_chunk_fwd needs for these shapes (pointers are not read).
- * Depends on B, T, H, Dk, Dv, dtype and on whether cu_seqlens is set (and N). */
+/* Workspace bytes kda_chunk_fwd needs for these shapes (pointers are not read,
+ * except that a fusion struct with conv_width > 0 adds room for the prologue's
+ * q, k, v, beta).  Depends on B, T, H, Dk, Dv, dtype, on whether cu_seqlens is
+ * set (and N) and on whether the prologue is on. */
 KDA_API kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args_t *args, size_t *bytes);
 
 KDA_API kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *args, void *stream);
