@@ -69,7 +69,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     __shared__ float s_o[FT][FV], s_gt[FT][FV];           // o~ and Sigmoid(gate) of the block (epilogue)
     __shared__ float s_hist[FU ? 3 : 1][FU ? CC : 1];     // conv history between blocks (prologue)
 
-    const int t = threadIdx.x, l = t & 63, w = t >> 6;
+    // (the fused variant keeps the wave index in a scalar: its per-wave LDS slots
+    // then need no per-lane address registers)
+    const int t = threadIdx.x, l = t & 63, w = FU ? __builtin_amdgcn_readfirstlane(t >> 6) : t >> 6;
     const int hf = l / CPW;                       // which 64 rows of the column
     const int col = w * CPW + (l % CPW);          // this lane's column
     const size_t nh = blockIdx.x;                 // sequence * H + head
@@ -130,6 +132,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
             constexpr int CPT = (DV + NT - 1) / NT;  // staged value columns per thread
             static_assert(!FU || (RPT == 1 && CPT == 1), "prologue staging assumes one row and one column per thread");
             T gz[TB][RPT], kk[TB][RPT], qq[TB][RPT], vr[TB][CPT], bt[TB], gl[FT][CPT];
+            // The thread index, opaque to the compiler inside this block: the
+            // per-thread addresses are recomputed here instead of being hoisted out
+            // of the block loop and kept live beside the state.
+            int tl = t;
+            if constexpr (FU) asm volatile("" : "+v"(tl));
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
                 const int it = base + j;
@@ -138,7 +145,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
                 const T *qsrc = rep ? (pro ? (const T *)p.q_r : nullptr) : (const T *)p.q;
 #pragma unroll
                 for (int i = 0; i < RPT; ++i) {
-                    const int r = t + i * NT;
+                    const int r = tl + i * NT;
                     const bool rk = ok && r < DK;
                     gz[j][i] = rk ? ((const T *)(rep ? p.g_r : p.g))[row * DK + r] : from_f<T>(0.f);
                     kk[j][i] = rk ? ((const T *)(rep ? p.k_r : p.k))[row * DK + r] : from_f<T>(0.f);
@@ -146,20 +153,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
                 }
 #pragma unroll
                 for (int i = 0; i < CPT; ++i) {
-                    const int cc = t + i * NT;
+                    const int cc = tl + i * NT;
                     vr[j][i] = (ok && cc < DV) ? ((const T *)(rep ? p.v_r : p.v))[row * DV + cc] : from_f<T>(0.f);
                     if constexpr (FU)
                         gl[j][i] = (epi && ok && !rep && cc < DV) ? ((const T *)p.f.gate)[row * DV + cc] : from_f<T>(0.f);
                 }
-                bt[j] = (ok && t == 0) ? ((const T *)(rep ? p.beta_r : p.beta))[row] : from_f<T>(0.f);
+                bt[j] = (ok && tl == 0) ? ((const T *)(rep ? p.beta_r : p.beta))[row] : from_f<T>(0.f);
             }
             float wq[4] = {0.f, 0.f, 0.f, 0.f}, wk[4] = {0.f, 0.f, 0.f, 0.f}, wv[4] = {0.f, 0.f, 0.f, 0.f};
             float hq[3] = {0.f, 0.f, 0.f}, hk[3] = {0.f, 0.f, 0.f}, hv[3] = {0.f, 0.f, 0.f};
-            // The thread index, opaque to the compiler inside this block: the
-            // prologue's per-thread addresses are recomputed here instead of being
-            // hoisted out of the block loop and kept live beside the state.
-            int tl = t;
-            if constexpr (FU) asm volatile("" : "+v"(tl));
             if constexpr (FU) {
                 if (pro) {
 #pragma unroll
@@ -349,10 +351,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
                 for (int x = 0; x < NW; ++x) kq += s_kqw[x][j];
                 if constexpr (FU) kq *= nk * nq;
                 const float ot = p.scale * (rr + d * kq);
-                if (FU && epi)
-                    s_o[FU ? j : 0][FU ? col : 0] = ot;
-                else
+                if (FU && epi) {
+                    int cl = col;
+                    asm volatile("" : "+v"(cl));  // the address is formed here, not kept from before the loop
+                    s_o[FU ? j : 0][FU ? cl : 0] = ot;
+                } else {
                     ((T *)p.o)[row_of(it) * DV + col] = from_f<T>(ot);
+                }
             }
             const float du = FU ? d * nk : d;     // k = a_k / |a_k| in the update
 #pragma unroll
