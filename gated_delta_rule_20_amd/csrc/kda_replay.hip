@@ -142,14 +142,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
                 const int it = base + j;
                 const bool ok = j < nb, rep = it < n_rep;
                 const size_t row = ok ? row_of(it) : 0;
-                const T *qsrc = rep ? (pro ? (const T *)p.q_r : nullptr) : (const T *)p.q;
 #pragma unroll
                 for (int i = 0; i < RPT; ++i) {
                     const int r = tl + i * NT;
                     const bool rk = ok && r < DK;
                     gz[j][i] = rk ? ((const T *)(rep ? p.g_r : p.g))[row * DK + r] : from_f<T>(0.f);
                     kk[j][i] = rk ? ((const T *)(rep ? p.k_r : p.k))[row * DK + r] : from_f<T>(0.f);
-                    qq[j][i] = (rk && qsrc) ? qsrc[row * DK + r] : from_f<T>(0.f);
+                    if constexpr (FU)  // with the prologue the replayed queries feed the convolution
+                        qq[j][i] = (rk && (pro || !rep)) ? ((const T *)(rep ? p.q_r : p.q))[row * DK + r] : from_f<T>(0.f);
+                    else
+                        qq[j][i] = (rk && !rep) ? ((const T *)p.q)[row * DK + r] : from_f<T>(0.f);
                 }
 #pragma unroll
                 for (int i = 0; i < CPT; ++i) {
