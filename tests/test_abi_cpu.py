@@ -294,3 +294,34 @@ def test_decode_fusion_width_one_needs_no_state(lib):
     a.N, a.H, a.Dk, a.Dv, a.dtype, a.g_min = 0, 2, 128, 128, kda.KDA_BF16, -5.0
     a.fusion = ctypes.pointer(f)
     assert lib.kda_recurrent_step(ctypes.byref(a), None) == 0
+
+
+def test_prefill_fusion_rejects_before_launch(lib):
+    """kda_chunk_fwd's fusion checks: overlapping convolution states, convolution
+    checkpoints without state checkpoints, a missing norm weight."""
+    ws = 1 << 20
+    for over, msg in [(dict(conv_state_out=0x40000), "overlaps"),
+                      (dict(conv_checkpoints=0x50000), "needs checkpoints"),
+                      (dict(gate=0x60000, o_norm_weight=None), "o_norm_weight is NULL"),
+                      (dict(conv_width=9), "conv_width=9")]:
+        f = _fusion(**over)
+        a = _args(workspace=0x1000000, workspace_bytes=1 << 34)
+        a.fusion = ctypes.pointer(f)
+        st = lib.kda_chunk_fwd(ctypes.byref(a), None)
+        assert st in (1, 2), (over, st)
+        assert msg in lib.kda_last_error_message().decode(), (over, lib.kda_last_error_message())
+    del ws
+
+
+def test_prologue_workspace_grows(lib):
+    """The fused prologue adds its convolved q, k, v, beta to the workspace:
+    rows*H*(2*Dk + Dv) + rows*H elements, each array 256-byte aligned."""
+    st, base = _ws(lib, _args())
+    f = _fusion()
+    a = _args()
+    a.fusion = ctypes.pointer(f)
+    out = ctypes.c_size_t(0)
+    assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(out)) == 0
+    rows, H = 128, 2
+    al = lambda b: (b + 255) // 256 * 256
+    assert out.value == base + 2 * al(rows * H * 128 * 2) + al(rows * H * 128 * 2) + al(rows * H * 2)
