@@ -1,0 +1,92 @@
+"""The fused layer (eq. (2) prologue, eq. (6) epilogue) at the full workload
+sizes, in the configuration the benchmark times: prefill_8k shapes (one call
+over B=1, T=8192, H=32, d=128 from pre-convolution projections) and decode_512
+shapes (512 sequences x 32 heads, consecutive steps, states in place).  The
+layer oracle recomputes sampled heads / sequences in full.
+
+The bf16 prefill output is checked as in test_gpu_fusion_prefill: o~ (the same
+call without the epilogue) against the oracle, and the fused output against the
+fp64 epilogue of that o~."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.layer as L
+import workloads as W
+from kda_testutil import TOL, np64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+QK_EPS, O_EPS, EPI_TOL = 1e-6, 1e-6, 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_20_amd as kda
+    kda.load_library()
+
+
+def test_layer_prefill_8k_sampled_heads():
+    import gated_delta_rule_20_amd as kda
+    w = W.WORKLOADS["prefill_8k"]
+    d = W.make_layer(w, "cuda", N=w.B, T=w.T, H=w.H)
+    heads = [0, 13, 31]
+
+    def run(epi):
+        cs_out = torch.empty_like(d["conv_state"])
+        f = kda.Fusion(conv_weight=d["conv_weight"], conv_state=d["conv_state"], conv_state_out=cs_out,
+                       qk_eps=QK_EPS, gate=d["gate"] if epi else None,
+                       o_norm_weight=d["o_norm_weight"] if epi else None, o_eps=O_EPS)
+        o, hT = kda.chunk_fwd(d["q_pre"], d["k_pre"], d["v_pre"], d["z"], d["beta_logit"], A_log=d["A_log"],
+                              g_min=d["g_min"], initial_state=d["state"], fusion=f)
+        torch.cuda.synchronize()
+        return o, hT, cs_out
+
+    y, hT, cs = run(True)
+    o_plain, _, _ = run(False)
+    sel = lambda t: np64(t[:, :, heads])                     # [B, T, H, .] -> sampled heads
+    o_ref, h_ref, cs_ref = L.layer_forward(
+        sel(d["q_pre"]), sel(d["k_pre"]), sel(d["v_pre"]), sel(d["z"]), sel(d["beta_logit"]),
+        conv_weight=np64(d["conv_weight"])[heads], conv_state=np64(d["conv_state"])[:, heads],
+        h0=np64(d["state"])[:, heads], A_log=np64(d["A_log"])[heads], g_min=d["g_min"], qk_eps=QK_EPS,
+        nthreads=16)
+    e_o = rel_err(np64(o_plain)[:, :, heads], o_ref)
+    e_s = rel_err(np64(hT)[:, heads], h_ref)
+    e_y = rel_err(np64(y)[:, :, heads], L.epilogue(np64(o_plain)[:, :, heads], np64(d["gate"])[:, :, heads],
+                                                   np64(d["o_norm_weight"])[heads], O_EPS))
+    print(f"o~ {e_o:.3e}  state {e_s:.3e}  epilogue {e_y:.3e}")
+    assert e_o <= TOL[torch.bfloat16] and e_s <= TOL[torch.bfloat16] and e_y <= EPI_TOL
+    assert np.array_equal(np64(cs)[:, heads], cs_ref)
+
+
+def test_layer_decode_512_sampled_sequences():
+    import gated_delta_rule_20_amd as kda
+    w = W.WORKLOADS["decode_512"]
+    K = 4
+    d = W.make_layer(dataclasses.replace(w, A_uniform=1.0), "cuda", N=w.B, T=K, H=w.H)
+    h0, cs0 = d["state"].clone(), d["conv_state"].clone()
+    state, cs = d["state"], d["conv_state"]
+    ys = []
+    for t in range(K):
+        sl = lambda n: d[n][:, t].contiguous()
+        f = kda.Fusion(conv_weight=d["conv_weight"], conv_state=cs, qk_eps=QK_EPS, gate=sl("gate"),
+                       o_norm_weight=d["o_norm_weight"], o_eps=O_EPS)
+        ys.append(kda.recurrent_step(sl("q_pre"), sl("k_pre"), sl("v_pre"), sl("z"), sl("beta_logit"), state,
+                                     A_log=d["A_log"], g_min=d["g_min"], fusion=f))
+    torch.cuda.synchronize()
+    seqs = [0, 1, 255, 511]
+    sel = lambda n: np64(d[n][seqs])
+    o_ref, h_ref, cs_ref = L.layer_forward(
+        sel("q_pre"), sel("k_pre"), sel("v_pre"), sel("z"), sel("beta_logit"),
+        conv_weight=np64(d["conv_weight"]), conv_state=np64(cs0[seqs]), h0=np64(h0[seqs]),
+        A_log=np64(d["A_log"]), g_min=d["g_min"], qk_eps=QK_EPS, gate=np64(d["gate"][seqs]),
+        o_weight=np64(d["o_norm_weight"]), o_eps=O_EPS, nthreads=16)
+    e_o = rel_err(np64(torch.stack(ys, 1)[seqs]), o_ref)
+    e_s = rel_err(np64(state[seqs]), h_ref)
+    print(f"y {e_o:.3e}  state {e_s:.3e}")
+    assert e_o <= TOL[torch.bfloat16] and e_s <= TOL[torch.bfloat16]
+    assert np.array_equal(np64(cs[seqs]), cs_ref)
