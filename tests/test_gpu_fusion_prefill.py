@@ -194,3 +194,53 @@ def test_fused_prefill_then_decode():
     assert rel_err(np64(torch.stack(ys, 1)), o_ref[:, T:]) <= TOL[torch.bfloat16]
     assert rel_err(np64(state), h_ref) <= TOL[torch.bfloat16]
     assert np.array_equal(np64(cs), cs_ref)
+
+
+def test_fused_prefill_packed_checkpoints_logdecay_deterministic():
+    """Packed sequences with state and convolution checkpoints every 64 tokens, in
+    log-decay mode (A_log = NULL); each written slot against the layer run over
+    that prefix of its sequence; two runs bitwise equal."""
+    import gated_delta_rule_20_amd as kda
+    lens = [130, 64, 200, 5, 129]
+    N, H, slots = len(lens), 2, 3
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    d = W.make_layer(_wl(seed=85), "cuda", N=1, T=int(cu[-1]), H=H)
+    d2 = W.make_layer(_wl(seed=86), "cuda", N=N, T=1, H=H)
+    flat = {n: d[n][0] for n in ("q_pre", "k_pre", "v_pre", "beta_logit", "gate")}
+    flat["z"] = (-5.0 * torch.rand(d["z"][0].shape, device="cuda")).to(torch.bfloat16)  # log-decays in [-5, 0]
+    flat.update(conv_weight=d["conv_weight"], o_norm_weight=d["o_norm_weight"], A_log=None, g_min=d["g_min"])
+    cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
+
+    def run():
+        ck = torch.full((N, slots, H, 128, 128), float("nan"), device="cuda")
+        cck = torch.full((N, slots, H, 3, 384), float("nan"), device="cuda", dtype=torch.bfloat16)
+        f = _fusion(flat, True, False, conv_state=d2["conv_state"], conv_checkpoints=cck)
+        o, hT = kda.chunk_fwd(flat["q_pre"], flat["k_pre"], flat["v_pre"], flat["z"], flat["beta_logit"],
+                              cu_seqlens=cu_t, initial_state=d2["state"], checkpoints=ck, checkpoint_every=1,
+                              fusion=f)
+        torch.cuda.synchronize()
+        return o, hT, ck, cck
+
+    o, hT, ck, cck = run()
+    o2, hT2, ck2, cck2 = run()
+    assert torch.equal(o, o2) and torch.equal(hT, hT2)
+    assert torch.equal(torch.nan_to_num(ck, 7.0), torch.nan_to_num(ck2, 7.0))
+    assert torch.equal(torch.nan_to_num(cck.float(), 7.0), torch.nan_to_num(cck2.float(), 7.0))
+    names = ("q_pre", "k_pre", "v_pre", "z", "beta_logit")
+    for s in range(N):
+        for j in range(slots):
+            P = (j + 1) * 64
+            if P >= lens[s]:
+                assert torch.isnan(ck[s, j]).all() and torch.isnan(cck[s, j].float()).all(), (s, j)
+                continue
+            a = int(cu[s])
+            _, h_ref, cs_ref = L.layer_forward(*[np64(flat[n][a:a + P]) for n in names],
+                                               conv_weight=np64(d["conv_weight"]),
+                                               conv_state=np64(d2["conv_state"][s:s + 1]),
+                                               h0=np64(d2["state"][s:s + 1]), A_log=None, g_min=d["g_min"],
+                                               qk_eps=QK_EPS)
+            assert rel_err(np64(ck[s, j]), h_ref[0]) <= TOL[torch.bfloat16], (s, j)
+            assert np.array_equal(np64(cck[s, j]), cs_ref[0]), (s, j)
+    o_ref, h_ref, _ = _ref(flat, True, False, cu=cu, conv_state=d2["conv_state"], h0=d2["state"])
+    assert rel_err(np64(o), o_ref) <= TOL[torch.bfloat16]
+    assert rel_err(np64(hT), h_ref) <= TOL[torch.bfloat16]
