@@ -153,6 +153,14 @@ __device__ __forceinline__ float gate_from_logit(float z, float eA, float g_min)
     return g_min / (1.0f + __expf(-x));
 }
 
+// 1 / sqrt(x) for the L2Norm / RMSNorm denominators (x = sum or mean of squares
+// plus a non-negative epsilon) on the hardware reciprocal square root; x is
+// raised to the smallest normal float first, so a zero vector with epsilon 0
+// gives 0 instead of 0 * inf.
+__device__ __forceinline__ float rsq_norm(float x) {
+    return __builtin_amdgcn_rsqf(fmaxf(x, 1.17549435e-38f));
+}
+
 __device__ __forceinline__ float clamp_logdecay(float g, float g_min) {
     return fminf(fmaxf(g, g_min), 0.0f);
 }

@@ -1081,7 +1081,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrefillParams p)
         for (int sidx = 0; sidx < 2; ++sidx) {
 #pragma unroll
             for (int r = 0; r < HW; ++r) {
-                const float n = rsqrtf(tot[sidx * HW + r] + p.f.qk_eps);
+                const float n = rsq_norm(tot[sidx * HW + r] + p.f.qk_eps);
                 ku o;
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) o[cc] = from_f<T>(a[sidx][r][cc] * n);
@@ -1162,7 +1162,7 @@ __global__ __launch_bounds__(256) void gate_norm_kernel(T *o, const T *gate, con
     for (int e = 0; e < VPL; ++e) ss += to_f<T>(ov[e]) * to_f<T>(ov[e]);
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
-    const float r = rsqrtf(ss * (1.f / DV) + eps);
+    const float r = rsq_norm(ss * (1.f / DV) + eps);
     const float *wr = wgt + (size_t)h * DV + c0;
 #pragma unroll
     for (int e = 0; e < VPL; ++e)

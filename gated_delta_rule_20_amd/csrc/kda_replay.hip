@@ -315,8 +315,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
                         a += s_sk[x][j];
                         b += s_sq[x][j];
                     }
-                    nk = rsqrtf(a + p.f.qk_eps);
-                    nq = rsqrtf(b + p.f.qk_eps);
+                    nk = rsq_norm(a + p.f.qk_eps);
+                    nq = rsq_norm(b + p.f.qk_eps);
                 }
             }
             float pp = 0.f, rr = 0.f;
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
 #pragma unroll
                     for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
                     if (te < DV) {
-                        const float y = s_gt[j][te] * wo * s_o[j][te] * rsqrtf(ss * (1.f / DV) + p.f.o_eps);
+                        const float y = s_gt[j][te] * wo * s_o[j][te] * rsq_norm(ss * (1.f / DV) + p.f.o_eps);
                         ((T *)p.o)[row_of(base + j) * DV + te] = from_f<T>(y);
                     }
                 }

@@ -108,8 +108,10 @@ typedef enum {
  * per head and token (mean over the Dv channels of the recurrence output o~).
  *   gate          : logits W_g x, shaped like o, in the call's dtype.
  *   o_norm_weight : [H, Dv] float32, required with gate.
- * Both epsilons must be >= 0.  A NULL fusion pointer (or conv_width = 0 and
- * gate = NULL) leaves every entry point exactly as documented above it.
+ * Both epsilons must be >= 0; with an epsilon of 0, a sum (or mean) of squares
+ * below 2^-126 is taken as 2^-126 (so a zero vector stays zero).  A NULL fusion
+ * pointer (or conv_width = 0 and gate = NULL) leaves every entry point exactly
+ * as documented above it.
  */
 typedef struct {
     int32_t conv_width;            /* W in 1..4, or 0: no prologue */
