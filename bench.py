@@ -380,7 +380,7 @@ def main():
                          "of the benchmark contract is printed in mode 'all'")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: there is no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():

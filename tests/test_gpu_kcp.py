@@ -8,7 +8,7 @@ from zero.  Both are computed with the prefill path itself:
 and segments merged in order then re-run from their true entering state must
 reproduce the single pass.  The merge is done here in fp32 with torch on the
 device: on several GPUs it is the all-gather plus prefix merge of eq. (17),
-which this build describes but does not run."""
+which is not implemented here (one GPU)."""
 import dataclasses
 
 import pytest
