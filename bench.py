@@ -23,6 +23,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import statistics
 import sys
 import time
@@ -51,10 +52,36 @@ def decode_counts(N, H, Dk, Dv, elem=2):
     return N * H * (2 * Dk * Dv * 4 + elem * (3 * Dk + 2 * Dv) + elem), N * H * 7 * Dk * Dv
 
 
+_C_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
+def source_digest(files):
+    """First 16 hex digits of sha256 over the listed csrc files with comments
+    removed and whitespace collapsed (string literals kept), so that a change
+    to a comment does not retire a profile taken on the same code.  None if a
+    file is missing."""
+    h = hashlib.sha256()
+    for f in files:
+        src = os.path.join(ROOT, "gated_delta_rule_20_amd", "csrc", f)
+        if not os.path.exists(src):
+            return None
+        with open(src) as fh:
+            h.update(code_tokens(fh.read()).encode())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
+
+
+def code_tokens(text):
+    """C/C++ source with // and /* */ comments removed (string and character
+    literals kept as written) and every run of whitespace made one space."""
+    text = _C_TOKENS.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return " ".join(text.split())
+
+
 def profiled_traffic(name):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
     (copy-calibrated), read from profiles/hbm_traffic_pmc.txt.  Returns None
-    when the kernel sources no longer hash to the digest that was profiled."""
+    when the kernel sources no longer match the digest that was profiled."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -64,14 +91,8 @@ def profiled_traffic(name):
         fields = dict(kv.split("=", 1) for kv in line.split()[1:])
         if fields.get("name") != name:
             continue
-        h = hashlib.sha256()
-        for f in fields["files"].split(","):
-            src = os.path.join(ROOT, "gated_delta_rule_20_amd", "csrc", f)
-            if not os.path.exists(src):  # the profiled source is gone: the record is stale
-                return None
-            with open(src, "rb") as fh:
-                h.update(fh.read())
-        return int(fields["traffic_bytes"]) if h.hexdigest()[:16] == fields["digest"] else None
+        d = source_digest(fields["files"].split(","))
+        return int(fields["traffic_bytes"]) if d is not None and d == fields["digest"] else None
     return None
 
 

@@ -6,9 +6,10 @@
 //   eq. (4)  A = Tril[(Q*Gamma)(K/Gamma)^T] (diagonal kept) and
 //            O = (Gamma*Q) S + A V~;
 //   "UT transform"  U, W with pseudo-values V~ = U - W S;
-//   eq. (5)  lower-bounded gate: a 16-token sub-tile spans a log-decay of at
-//            most 15*|g_min| <= 75, so its rescale factors stay inside the
-//            bf16/fp32 range ("lower-bounded decay" paragraph and Fig. 3).
+//   eq. (5)  lower-bounded gate: g > g_min = -5, so the log-decay summed over
+//            a 16-token sub-tile lies in (-80, 0] and its reciprocal rescale
+//            factors stay below e^80, inside the bf16/fp32 range
+//            ("lower-bounded decay" paragraph and Fig. 3).
 // U, W and the hand-off between chunks are not printed on the page; unrolling
 // eq. (1) over one chunk entered with state S gives
 //   L     = StrictTril(Diag(beta) K+ K-^T),   K+ = K*Gamma, K- = K/Gamma
@@ -33,13 +34,12 @@
 //                        Columns of S evolve independently (V~ = U - W S acts
 //                        column by column), which licenses the split.
 //
-// Sub-tile references.  For rows r in 16-token tile m and columns i in tile
-// n <= m, exp(lam_r - lam_i) is factored at b = 16n (first token of tile n):
-// exp(lam_r - lam_b) <= 1 times exp(lam_b - lam_i) in [1, e^75].  Row
-// operands are stored relative to their own tile start, exp(lam_r - lam_16m),
-// and multiplied by the per-channel factor exp(lam_16m - lam_16n) <= 1 for
-// off-diagonal tiles, so no factor overflows; a factor that underflows
-// belongs to a product below e^-12 times its operands.
+// Sub-tile references.  Let B_m be lam just before 16-token tile m (B_0 = 0).
+// For rows r in tile m and columns i in tile n <= m, exp(lam_r - lam_i) is
+// factored at B_m: the row operand exp(lam_r - B_m) in [e^-80, 1] times the
+// column operand exp(B_m - lam_i), which lies in [1, e^80] for n = m and is
+// <= 1 for n < m.  No factor overflows; a column factor that underflows
+// belongs to a product exp(lam_r - lam_i) below the smallest normal float.
 #include "kda_common.h"
 #include "kda_prefill.h"
 
@@ -128,17 +128,18 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t *__rest
 }
 
 // -----------------------------------------------------------------------------
-// Intra-chunk stage.  256 threads = 4 waves.  The grid is persistent: each
+// Intra-chunk stage.  512 threads = 8 waves.  The grid is persistent: each
 // workgroup walks (chunk, head) items with a stride of gridDim.x, from the
 // last chunk to the first (the blocks the chain kernel reads first are
 // written last and are the likeliest to still sit in the last-level cache),
 // and the raw inputs of its next item are loaded into registers while the
 // current item is computed.
 //
-// Elementwise layout: wave w owns 16-token sub-tile w and lane l owns the CPT
-// channels CPT*l.. (CPT = d_k/64) across all 16 tokens, so the chunk-local
-// cumsum runs inside each thread and only the four tile totals are
-// exchanged.  Log-decays are kept in log2 units (one exp2 per factor).
+// Elementwise layout: wave w owns 8 tokens of 16-token sub-tile w % 4 (the
+// first or second half, w / 4) and lane l owns the CPT channels CPT*l..
+// (CPT = d_k/64) across those 8 tokens, so the chunk-local cumsum runs inside
+// each thread and only the eight half-tile totals are exchanged.  Log-decays
+// are kept in log2 units (one exp2 per factor).
 //
 // Sub-tile references.  Let B_m be lam just before tile m (B_0 = 0) and
 // T_m = B_{m+1} - B_m <= 0 the tile's total.  Row operands carry

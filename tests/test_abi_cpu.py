@@ -221,6 +221,16 @@ def test_bench_traffic_records_parse():
     assert bench.profiled_traffic("no-such-kernel") is None
 
 
+def test_bench_source_digest_ignores_comments_only():
+    """The digest that keys the traffic records sees code, not comments or layout."""
+    import bench
+    a = 'int f(int x) { // scale\n  return 2 * x; /* twice */ }\nconst char *s = "a // b /* c */";'
+    assert bench.code_tokens(a) == 'int f(int x) { return 2 * x; }\nconst char *s = "a // b /* c */";'.replace("\n", " ")
+    assert bench.code_tokens("/* one // two */ x;\n// y */\nz;") == "x; z;"
+    assert bench.code_tokens(a) != bench.code_tokens(a.replace("2 * x", "3 * x"))
+    assert bench.source_digest(["no_such_file.hip"]) is None
+
+
 def test_binding_shape_checks():
     """The binding rejects mismatched operand shapes before any launch."""
     import torch

@@ -100,6 +100,17 @@ def test_varlen_small():
     _check(inp)
 
 
+def test_varlen_many_sequences():
+    """2100 packed sequences, past the 2048 up to which the chunk table sorts
+    sequences longest first (beyond it they keep their given order): lengths
+    0..39 with 40 at or around one and two chunks."""
+    r = np.random.default_rng(31)
+    lengths = r.integers(0, 40, size=2100)
+    lengths[r.choice(2100, 40, replace=False)] = r.choice([63, 64, 65, 128, 129], 40)
+    inp = _small("varlen_64", H=2, seed=31, lengths=lengths.tolist())
+    _check(inp)
+
+
 def test_query_scale():
     inp = _small("prefill_8k", T=150, H=2, seed=12)
     inp["scale"] = 0.0883883476
