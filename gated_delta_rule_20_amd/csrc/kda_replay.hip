@@ -416,13 +416,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     }
 }
 
+// The plain single decode step is bound by HBM.  Its registers allow three
+// resident workgroups per CU; two keep fewer state streams in flight at once,
+// which the HBM serves faster (about 1% per step at 512 x 32 heads of
+// 128 x 128; one per CU is far slower).  An unused dynamic LDS allocation caps
+// residency at two: with the kernel's static LDS (1.5 to 3 KiB) each workgroup
+// holds 57.5 to 59 KiB, more than a third of the CU's 160 KiB and less than
+// the 64 KiB a launch may take without raising its limit.  The fused variant
+// does more VALU work per state element and the windowed variant more work per
+// state read: both run best at three and launch without the pad.
+constexpr size_t kDecodeOccupancyPad = 56 * 1024;
+
 template <typename T, int DK, int DV, bool FU>
 static void launch_replay_tb(const ReplayParams &p, hipStream_t stream)
 {
     const unsigned grid = (unsigned)((size_t)p.N * p.H);
     const dim3 block(DV * (DK / 64));
     if (p.T_replay + p.T_new == 1)  // one token per sequence: the single decode step
-        hipLaunchKernelGGL((replay_kernel<T, DK, DV, 1, FU>), dim3(grid), block, 0, stream, p);
+        hipLaunchKernelGGL((replay_kernel<T, DK, DV, 1, FU>), dim3(grid), block, FU ? 0 : kDecodeOccupancyPad,
+                           stream, p);
     else
         hipLaunchKernelGGL((replay_kernel<T, DK, DV, 8, FU>), dim3(grid), block, 0, stream, p);
 }
