@@ -23,13 +23,81 @@
 
 namespace kda {
 
+// Row-broadcast FMAs.  Lane l holds row 16 V + (l % 16) of a per-row operand
+// in kr; DPP row_newbcast:n hands every lane of a 16-lane row the value of
+// its lane n, so 16 FMAs cover 16 rows with no further LDS reads and in the
+// same order, with the same roundings, as the broadcast-read loop.  A DPP
+// read of a VGPR needs two wait states after a VALU write of it and five after
+// a VALU write of EXEC, which the compiler does not insert around inline
+// assembly: each group starts with s_nop W (W + 1 wait states), W = 4 where
+// EXEC may just have changed.
+//   dot16: acc += sum over n of kr[row 16 V + n] * x[16 V + n]
+//   upd16: x[16 V + n] += kr[row 16 V + n] * d
+template <int V, int W = 1> __device__ __forceinline__ void dot16(float &acc, float kr, const float *x)
+{
+    asm("s_nop %c18\n"
+        "v_fmac_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %7 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %8 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %9 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %10 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %11 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %12 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %13 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %14 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %15 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %16 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %17 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+        : "+v"(acc)
+        : "v"(kr),
+          "v"(x[16 * V + 0]), "v"(x[16 * V + 1]), "v"(x[16 * V + 2]), "v"(x[16 * V + 3]),
+          "v"(x[16 * V + 4]), "v"(x[16 * V + 5]), "v"(x[16 * V + 6]), "v"(x[16 * V + 7]),
+          "v"(x[16 * V + 8]), "v"(x[16 * V + 9]), "v"(x[16 * V + 10]), "v"(x[16 * V + 11]),
+          "v"(x[16 * V + 12]), "v"(x[16 * V + 13]), "v"(x[16 * V + 14]), "v"(x[16 * V + 15]),
+          "i"(W));
+}
+template <int V, int W = 1> __device__ __forceinline__ void upd16(float *x, float kr, float d)
+{
+    asm("s_nop %c18\n"
+        "v_fmac_f32_dpp %0, %16, %17 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %1, %16, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %2, %16, %17 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %3, %16, %17 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %4, %16, %17 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %5, %16, %17 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %6, %16, %17 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %7, %16, %17 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %8, %16, %17 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %9, %16, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %10, %16, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %11, %16, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %12, %16, %17 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %13, %16, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %14, %16, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %15, %16, %17 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+        : "+v"(x[16 * V + 0]), "+v"(x[16 * V + 1]), "+v"(x[16 * V + 2]), "+v"(x[16 * V + 3]),
+          "+v"(x[16 * V + 4]), "+v"(x[16 * V + 5]), "+v"(x[16 * V + 6]), "+v"(x[16 * V + 7]),
+          "+v"(x[16 * V + 8]), "+v"(x[16 * V + 9]), "+v"(x[16 * V + 10]), "+v"(x[16 * V + 11]),
+          "+v"(x[16 * V + 12]), "+v"(x[16 * V + 13]), "+v"(x[16 * V + 14]), "+v"(x[16 * V + 15])
+        : "v"(kr), "v"(d), "i"(W));
+}
+
 // One workgroup per (sequence, head).  Each state column is held by NH = d_k/64
 // lanes of one wave (lanes l and l + 32 when NH = 2), each with 64 rows of it
 // in registers.  A token's two reductions over the rows, p = (D S)^T k and
 // r = (D S)^T q, are then sums inside each lane plus one lane swap, so the
-// token loop needs no barrier; the per-row operands are read from LDS as
-// broadcasts, four rows per read.  Token inputs are staged TB tokens at a time
-// (all loads in flight together); TB = 1 is the single decode step.
+// token loop needs no barrier.  The per-row operands of a token come from LDS:
+// in the single step and the fused variant as broadcasts, four rows per read;
+// in the plain multi-token variant each lane reads a 16-row slice of each
+// operand once per token and every FMA takes its row from the lane that holds
+// it (DPP row broadcast, below).  That variant needs 128 VGPRs and runs four
+// workgroups per CU, which its per-token VALU work needs to overlap the state
+// traffic.  Token inputs are staged TB tokens at a time (all loads in flight
+// together); TB = 1 is the single decode step.
 //
 // Decay folding.  Inside a block the registers hold the state in a scaled
 // frame, X = S / P_j with P_j the per-row product of alpha over the block's
@@ -52,7 +120,7 @@ namespace kda {
 // the block, each wave sums o~^2 over the head's d_v columns for each token and
 // the thread of column c writes Sigmoid(gate) * w_c * o~_c / rms.
 template <typename T, int DK, int DV, int TB, bool FU>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void replay_kernel(ReplayParams p)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TB > 1 && !FU) ? 4 : 3))) void replay_kernel(ReplayParams p)
 {
     constexpr int NH = DK / 64;         // lanes per column
     constexpr int RH = 64;              // rows per lane
@@ -60,6 +128,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     constexpr int NT = DV * NH;         // threads
     constexpr int NW = NT / 64;         // waves
     constexpr int CC = 2 * DK + DV;     // convolution channels per head
+    constexpr bool RB = TB > 1 && !FU;  // row-broadcast token loop
     static_assert(NH * RH == DK && NT % 64 == 0 && NT <= 256 && NT >= DK && NT >= DV, "shape");
     __shared__ __align__(16) float s_kd[TB][DK], s_qd[TB][DK], s_ki[TB][DK];  // P_j k, P_j q, k / P_j
     __shared__ __align__(16) float s_pc[DK], s_pe[DK];    // P at the commit token, P at the block end
@@ -320,23 +389,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
                 }
             }
             float pp = 0.f, rr = 0.f;
+            if constexpr (RB) {
+                float kv[4], qv[4];           // rows r0h + 16 v + (l % 16)
 #pragma unroll
-            for (int g0 = 0; g0 < RH; g0 += GR) {
-#pragma unroll
-                for (int r = g0; r < g0 + GR; r += 4) {
-                    const f32x4 k4 = *reinterpret_cast<const f32x4 *>(kd + r);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) pp += st[r + e] * k4[e];
+                for (int v = 0; v < 4; ++v) {
+                    kv[v] = kd[16 * v + (l & 15)];
+                    qv[v] = rep ? 0.f : qd[16 * v + (l & 15)];
                 }
+                dot16<0, 4>(pp, kv[0], st); dot16<1>(pp, kv[1], st); dot16<2>(pp, kv[2], st); dot16<3>(pp, kv[3], st);
                 if (!rep) {
+                    dot16<0, 4>(rr, qv[0], st); dot16<1>(rr, qv[1], st); dot16<2>(rr, qv[2], st);
+                    dot16<3>(rr, qv[3], st);
+                }
+            } else {
+#pragma unroll
+                for (int g0 = 0; g0 < RH; g0 += GR) {
 #pragma unroll
                     for (int r = g0; r < g0 + GR; r += 4) {
-                        const f32x4 q4 = *reinterpret_cast<const f32x4 *>(qd + r);
+                        const f32x4 k4 = *reinterpret_cast<const f32x4 *>(kd + r);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) rr += st[r + e] * q4[e];
+                        for (int e = 0; e < 4; ++e) pp += st[r + e] * k4[e];
                     }
+                    if (!rep) {
+#pragma unroll
+                        for (int r = g0; r < g0 + GR; r += 4) {
+                            const f32x4 q4 = *reinterpret_cast<const f32x4 *>(qd + r);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) rr += st[r + e] * q4[e];
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
             if (NH == 2) {                        // the other 64 rows of the column
                 pp += __shfl_xor(pp, 32);
@@ -362,15 +445,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
                 }
             }
             const float du = FU ? d * nk : d;     // k = a_k / |a_k| in the update
+            if constexpr (RB) {
+                float iv[4];
 #pragma unroll
-            for (int g0 = 0; g0 < RH; g0 += GR) {
+                for (int v = 0; v < 4; ++v) iv[v] = ki[16 * v + (l & 15)];
+                // EXEC may have changed for the output store just above
+                upd16<0, 4>(st, iv[0], du); upd16<1>(st, iv[1], du); upd16<2>(st, iv[2], du); upd16<3>(st, iv[3], du);
+            } else {
 #pragma unroll
-                for (int r = g0; r < g0 + GR; r += 4) {
-                    const f32x4 i4 = *reinterpret_cast<const f32x4 *>(ki + r);
+                for (int g0 = 0; g0 < RH; g0 += GR) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) st[r + e] += i4[e] * du;
+                    for (int r = g0; r < g0 + GR; r += 4) {
+                        const f32x4 i4 = *reinterpret_cast<const f32x4 *>(ki + r);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) st[r + e] += i4[e] * du;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
             if (j == jc) {                        // write back the true state X * P
 #pragma unroll
