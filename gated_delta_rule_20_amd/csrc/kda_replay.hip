@@ -90,14 +90,19 @@ template <int V, int W = 1> __device__ __forceinline__ void upd16(float *x, floa
 // lanes of one wave (lanes l and l + 32 when NH = 2), each with 64 rows of it
 // in registers.  A token's two reductions over the rows, p = (D S)^T k and
 // r = (D S)^T q, are then sums inside each lane plus one lane swap, so the
-// token loop needs no barrier.  The per-row operands of a token come from LDS:
-// in the single step and the fused variant as broadcasts, four rows per read;
-// in the plain multi-token variant each lane reads a 16-row slice of each
-// operand once per token and every FMA takes its row from the lane that holds
-// it (DPP row broadcast, below).  That variant needs 128 VGPRs and runs four
-// workgroups per CU, which its per-token VALU work needs to overlap the state
-// traffic.  Token inputs are staged TB tokens at a time (all loads in flight
-// together); TB = 1 is the single decode step.
+// token loop needs no barrier.  The per-row operands of a token come from LDS,
+// in one of two loops (RB below):
+//  * broadcast reads, four rows per read: the plain single step (HBM-bound;
+//    it runs best with few workgroups in flight) and the fused multi-token
+//    window (which spills at 128 VGPRs);
+//  * row broadcast: each lane reads a 16-row slice of each operand once per
+//    token and every FMA takes its row from the lane that holds it (DPP, see
+//    dot16 / upd16): the plain multi-token window and the fused single step.
+//    These fit in 128 VGPRs and run four workgroups per CU, which their extra
+//    VALU work per state element needs to overlap the state traffic.
+// Both loops run the same FMAs in the same order.  Token inputs are staged TB
+// tokens at a time (all loads in flight together); TB = 1 is the single decode
+// step.
 //
 // Decay folding.  Inside a block the registers hold the state in a scaled
 // frame, X = S / P_j with P_j the per-row product of alpha over the block's
@@ -120,7 +125,7 @@ template <int V, int W = 1> __device__ __forceinline__ void upd16(float *x, floa
 // the block, each wave sums o~^2 over the head's d_v columns for each token and
 // the thread of column c writes Sigmoid(gate) * w_c * o~_c / rms.
 template <typename T, int DK, int DV, int TB, bool FU>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TB > 1 && !FU) ? 4 : 3))) void replay_kernel(ReplayParams p)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(((TB > 1 && !FU) || (TB == 1 && FU)) ? 4 : 3))) void replay_kernel(ReplayParams p)
 {
     constexpr int NH = DK / 64;         // lanes per column
     constexpr int RH = 64;              // rows per lane
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TB > 1 && 
     constexpr int NT = DV * NH;         // threads
     constexpr int NW = NT / 64;         // waves
     constexpr int CC = 2 * DK + DV;     // convolution channels per head
-    constexpr bool RB = TB > 1 && !FU;  // row-broadcast token loop
+    constexpr bool RB = (TB > 1 && !FU) || (TB == 1 && FU);  // row-broadcast token loop
     static_assert(NH * RH == DK && NT % 64 == 0 && NT <= 256 && NT >= DK && NT >= DV, "shape");
     __shared__ __align__(16) float s_kd[TB][DK], s_qd[TB][DK], s_ki[TB][DK];  // P_j k, P_j q, k / P_j
     __shared__ __align__(16) float s_pc[DK], s_pe[DK];    // P at the commit token, P at the block end
