@@ -509,8 +509,8 @@ def main():
             "prefill": {"workload": f"prefill_8k shapes (B={B_} T={T_} H={H_} d={Dk_}) from pre-convolution "
                                     "projections, bf16", "ms_per_call": lp["ms"], "ms_median": lp["ms_median"],
                         "tokens_per_s": lp["tokens"] / (lp["ms"] / 1e3), "vs_core_call": lp["ms"] / pf["ms"],
-                        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd with fusion (intra_chunk_kernel "
-                                     "with prologue + chain_kernel + gate_norm_kernel)", "achieved": lp_gbs,
+                        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd with fusion (prologue_kernel + "
+                                     "intra_chunk_kernel + chain_kernel + gate_norm_kernel)", "achieved": lp_gbs,
                                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lp_gbs / HBM_PEAK_GBS,
                                      "traffic": profiled_traffic("layer_prefill"), "algorithmic_bytes": lp["bytes"]}},
             "decode": {"workload": f"decode_512 shapes (N={ld['N']} x 1 token, H={ld['H']}, d=128), fp32 state and "
