@@ -518,9 +518,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(((TB > 1 &&
 // 128 x 128; one per CU is far slower).  An unused dynamic LDS allocation caps
 // residency at two: with the kernel's static LDS (1.5 to 3 KiB) each workgroup
 // holds 57.5 to 59 KiB, more than a third of the CU's 160 KiB and less than
-// the 64 KiB a launch may take without raising its limit.  The fused variant
-// does more VALU work per state element and the windowed variant more work per
-// state read: both run best at three and launch without the pad.
+// the 64 KiB a launch may take without raising its limit.  The fused single
+// step and the windows do more VALU work per state element: they need more
+// workgroups in flight, not fewer, and launch without the pad.
 constexpr size_t kDecodeOccupancyPad = 56 * 1024;
 
 template <typename T, int DK, int DV, bool FU>
