@@ -319,6 +319,66 @@ def bench_layer_decode(warmup_rounds=1, steps=64):
                 N=N, H=H, bytes=layer_counts(N, N, H, Dk, Dv))
 
 
+def layer_spec_counts(N, H, Dk, Dv, n_replayed, T_new, W=4, elem=2):
+    """Algorithmic bytes of one fused replay call: the fp32 state and the
+    convolution state read and written once; per replayed token its q, k, v
+    projections, z and beta logit (q only feeds the convolution); per new token
+    the same plus the gate logits and the output; the filters once."""
+    C = 2 * Dk + Dv
+    state = 2 * N * H * Dk * Dv * 4 + 2 * N * H * (W - 1) * C * elem
+    replay = n_replayed * H * (2 * Dk + Dv + Dk + 1) * elem
+    new = N * T_new * H * (3 * Dk + 3 * Dv + 1) * elem
+    return state + replay + new + H * C * W * 4 + H * Dv * 4
+
+
+def bench_layer_spec(T_new=4, calls=16, warmup_rounds=1):
+    """decode_512_spec shapes through the fused layer: per call the accepted
+    drafts of a cached window are replayed and a new window (bonus + drafts)
+    runs, both from pre-convolution projections with the eq. (2) prologue and
+    the eq. (6) epilogue in the kernel; the recurrent and convolution states
+    are updated in place at the bonus token (fresh inputs per call)."""
+    w = W.WORKLOADS["decode_512_spec"]
+    Tr = w.T - 1
+    base = W.make_layer(w, "cuda", N=w.B, T=1, H=w.H)
+    state, cs = base["state"], base["conv_state"]
+    cpu = torch.Generator().manual_seed(w.seed + 7)
+    lo, hi = w.len_range
+    names = ("q_pre", "k_pre", "v_pre", "z", "beta_logit")
+    cl = []
+    for i in range(calls):
+        d = W.make_layer(w, "cuda", N=w.B, T=Tr + T_new, H=w.H, seed_offset=i + 1)
+        del d["state"]
+        x = {f"{n}_r": d[n][:, :Tr].contiguous() for n in names}
+        x.update({n: d[n][:, Tr:].contiguous() for n in names})
+        x["gate"] = d["gate"][:, Tr:].contiguous()
+        x["n_replay"] = torch.randint(lo, hi + 1, (w.B,), generator=cpu, dtype=torch.int32).to("cuda")
+        cl.append(x)
+        del d
+    fus = [kda.Fusion(conv_weight=base["conv_weight"], conv_state=cs, qk_eps=1e-6, gate=x["gate"],
+                      o_norm_weight=base["o_norm_weight"], o_eps=1e-6) for x in cl]
+    outs = [torch.empty_like(x["v_pre"]) for x in cl]
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        x = cl[i]
+        kda.recurrent_replay(x["q_pre"], x["k_pre"], x["v_pre"], x["z"], x["beta_logit"], state,
+                             replay=(x["k_pre_r"], x["v_pre_r"], x["z_r"], x["beta_logit_r"]),
+                             n_replay=x["n_replay"], n_commit=1, A_log=base["A_log"], g_min=base["g_min"],
+                             q_r=x["q_pre_r"], out=outs[i], stream=stream, fusion=fus[i])
+
+    for _ in range(warmup_rounds):
+        for i in range(calls):
+            call(i)
+    per_call, _ = time_calls(call, calls, stream)
+    N, T, H, Dk = cl[0]["q_pre"].shape
+    Dv = cl[0]["v_pre"].shape[-1]
+    n_rep = sum(int(x["n_replay"].sum()) for x in cl) / calls
+    us = 1e3 * sum(per_call) / len(per_call)
+    return dict(us=us, us_median=1e3 * statistics.median(per_call), us_min=1e3 * min(per_call), calls=calls,
+                N=N, H=H, T_new=T, T_replay=Tr, mean_replayed=n_rep / N,
+                bytes=layer_spec_counts(N, H, Dk, Dv, n_rep, T))
+
+
 def copy_calibration(steps, nbytes=1 << 30):
     """A plain device-to-device copy of known size (for scaling the HBM
     FETCH_SIZE / WRITE_SIZE counters: it reads and writes nbytes each)."""
@@ -421,7 +481,8 @@ def main():
     if args.mode == "layer":
         lp = bench_layer_prefill(args.steps, args.warmup)
         ld = bench_layer_decode()
-        print(json.dumps({"prefill_ms": lp["ms"], "decode_us": ld["us"]}))
+        ls = bench_layer_spec()
+        print(json.dumps({"prefill_ms": lp["ms"], "decode_us": ld["us"], "spec_us": ls["us"]}))
         return
 
     pf = bench_prefill(args.steps, args.warmup)
@@ -500,8 +561,10 @@ def main():
     if not args.no_layer:
         lp = bench_layer_prefill(args.steps, args.warmup)
         ld = bench_layer_decode()
+        ls = bench_layer_spec()
         lp_gbs = lp["bytes"] / (lp["ms"] / 1e3) / 1e9
         ld_gbs = ld["bytes"] / (ld["us"] / 1e6) / 1e9
+        ls_gbs = ls["bytes"] / (ls["us"] / 1e6) / 1e9
         B_, T_, H_, Dk_, Dv_ = lp["shape"]
         result["layer"] = {
             "what": "eq. (2) prologue (ShortConv width 4, Swish, L2Norm, Sigmoid beta) and eq. (6) epilogue "
@@ -521,6 +584,13 @@ def main():
                                     "achieved": ld_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": ld_gbs / HBM_PEAK_GBS, "traffic": profiled_traffic("layer_decode"),
                                     "algorithmic_bytes": ld["bytes"]}},
+            "spec": {"workload": f"decode_512_spec shapes (N={ls['N']}, H={ls['H']}, d=128): cached drafts "
+                                 f"{ls['T_replay']} (mean {ls['mean_replayed']:.2f} accepted and replayed), new "
+                                 f"window {ls['T_new']}, bonus committed, {ls['calls']} calls with fresh inputs",
+                     "us_per_call": ls["us"], "us_median": ls["us_median"], "us_min": ls["us_min"],
+                     "roofline": {"bound": "hbm", "kernel": "replay_kernel (fused variant)", "achieved": ls_gbs,
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ls_gbs / HBM_PEAK_GBS,
+                                  "traffic": profiled_traffic("layer_spec"), "algorithmic_bytes": ls["bytes"]}},
         }
         torch.cuda.empty_cache()
     if not args.no_other:

@@ -92,14 +92,14 @@ template <int V, int W = 1> __device__ __forceinline__ void upd16(float *x, floa
 // r = (D S)^T q, are then sums inside each lane plus one lane swap, so the
 // token loop needs no barrier.  The per-row operands of a token come from LDS,
 // in one of two loops (RB below):
-//  * broadcast reads, four rows per read: the plain single step (HBM-bound;
-//    it runs best with few workgroups in flight) and the fused multi-token
-//    window (which spills at 128 VGPRs);
-//  * row broadcast: each lane reads a 16-row slice of each operand once per
-//    token and every FMA takes its row from the lane that holds it (DPP, see
-//    dot16 / upd16): the plain multi-token window and the fused single step.
-//    These fit in 128 VGPRs and run four workgroups per CU, which their extra
-//    VALU work per state element needs to overlap the state traffic.
+//  * broadcast reads, four rows per read: the plain single step, which is
+//    HBM-bound and runs best with few workgroups in flight;
+//  * row broadcast, everywhere else: each lane reads a 16-row slice of each
+//    operand once per token and every FMA takes its row from the lane that
+//    holds it (DPP, see dot16 / upd16).  It frees registers: the plain window
+//    and the fused single step fit in 128 VGPRs and run four workgroups per CU,
+//    which their extra VALU work per state element needs to overlap the state
+//    traffic (the fused window would spill there and stays at three).
 // Both loops run the same FMAs in the same order.  Token inputs are staged TB
 // tokens at a time (all loads in flight together); TB = 1 is the single decode
 // step.
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(((TB > 1 &&
     constexpr int NT = DV * NH;         // threads
     constexpr int NW = NT / 64;         // waves
     constexpr int CC = 2 * DK + DV;     // convolution channels per head
-    constexpr bool RB = (TB > 1 && !FU) || (TB == 1 && FU);  // row-broadcast token loop
+    constexpr bool RB = TB > 1 || FU;  // row-broadcast token loop (all but the plain single step)
     static_assert(NH * RH == DK && NT % 64 == 0 && NT <= 256 && NT >= DK && NT >= DV, "shape");
     __shared__ __align__(16) float s_kd[TB][DK], s_qd[TB][DK], s_ki[TB][DK];  // P_j k, P_j q, k / P_j
     __shared__ __align__(16) float s_pc[DK], s_pe[DK];    // P at the commit token, P at the block end
