@@ -90,3 +90,44 @@ def test_layer_decode_512_sampled_sequences():
     print(f"y {e_o:.3e}  state {e_s:.3e}")
     assert e_o <= TOL[torch.bfloat16] and e_s <= TOL[torch.bfloat16]
     assert np.array_equal(np64(cs[seqs]), cs_ref)
+
+
+def test_layer_spec_512_sampled_sequences():
+    """decode_512_spec shapes through the fused layer, as the benchmark times them:
+    512 sequences x 32 heads, a cached 3-token window of which 0..3 drafts were
+    accepted and are replayed, then 4 new tokens, the bonus token committed.
+    Sampled sequences are recomputed by the layer oracle over (accepted drafts ++
+    new tokens); the committed states against its state after the bonus token."""
+    import gated_delta_rule_20_amd as kda
+    w = W.WORKLOADS["decode_512_spec"]
+    Tr, Tn = w.T - 1, 4
+    d = W.make_layer(dataclasses.replace(w, A_uniform=1.0), "cuda", N=w.B, T=Tr + Tn, H=w.H)
+    g = torch.Generator().manual_seed(77)
+    n_rep = torch.randint(0, Tr + 1, (w.B,), generator=g, dtype=torch.int32)
+    h0, cs0 = d["state"].clone(), d["conv_state"].clone()
+    state, cs = d["state"], d["conv_state"]
+    names = ("q_pre", "k_pre", "v_pre", "z", "beta_logit")
+    part = lambda n, a, b: d[n][:, a:b].contiguous()
+    q, k, v, z, b = (part(n, Tr, Tr + Tn) for n in names)
+    rq, rk, rv, rz, rb = (part(n, 0, Tr) for n in names)
+    f = kda.Fusion(conv_weight=d["conv_weight"], conv_state=cs, qk_eps=QK_EPS, gate=part("gate", Tr, Tr + Tn),
+                   o_norm_weight=d["o_norm_weight"], o_eps=O_EPS)
+    o = kda.recurrent_replay(q, k, v, z, b, state, replay=(rk, rv, rz, rb), n_replay=n_rep.cuda(), n_commit=1,
+                             A_log=d["A_log"], g_min=d["g_min"], q_r=rq, fusion=f)
+    torch.cuda.synchronize()
+    seqs = [0, 1, 300, 511]
+    for s in seqs:
+        nr = int(n_rep[s])
+        idx = list(range(nr)) + list(range(Tr, Tr + Tn))
+        ref = lambda toks: L.layer_forward(
+            *(np64(d[n][s:s + 1, toks]) for n in names), conv_weight=np64(d["conv_weight"]),
+            conv_state=np64(cs0[s:s + 1]), h0=np64(h0[s:s + 1]), A_log=np64(d["A_log"]), g_min=d["g_min"],
+            qk_eps=QK_EPS, gate=np64(d["gate"][s:s + 1, toks]), o_weight=np64(d["o_norm_weight"]), o_eps=O_EPS,
+            nthreads=16)
+        o_ref, _, _ = ref(idx)
+        _, h_ref, cs_ref = ref(list(range(nr)) + [Tr])       # committed: the accepted drafts and the bonus
+        e_o = rel_err(np64(o[s]), o_ref[0, nr:])
+        e_s = rel_err(np64(state[s]), h_ref[0])
+        print(f"seq {s} (replayed {nr}): y {e_o:.3e}  state {e_s:.3e}")
+        assert e_o <= TOL[torch.bfloat16] and e_s <= TOL[torch.bfloat16], (s, nr, e_o, e_s)
+        assert np.array_equal(np64(cs[s]), cs_ref[0]), s
