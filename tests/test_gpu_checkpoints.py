@@ -112,6 +112,30 @@ def test_resume_from_checkpoint():
     assert rel_err(np64(h2), np64(hT)) <= tol
 
 
+def test_checkpoints_prefill_8k_sampled_heads():
+    """prefill_8k at full size with a checkpoint every 8 chunks (512 tokens), the
+    configuration the benchmark times: outputs and final state bit-identical to the
+    call without checkpoints; slots 0, 7 and 14 (after 512, 4096 and 7680 tokens) of
+    three heads against the oracle over that prefix; slot 15 (the sequence end) not
+    written."""
+    inp = W.make_prefill(W.WORKLOADS["prefill_8k"], device="cuda")
+    o1, h1 = gpu_prefill(inp)
+    o2, h2, ck = _run_with_checkpoints(inp, every=8, slots=16)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    assert torch.isnan(ck[:, 15]).all()
+    heads = [0, 17, 31]
+    tol = TOL[inp["q"].dtype]
+    for j in (0, 7, 14):
+        pos = (j + 1) * 8 * 64
+        sub = dict(inp)
+        for key in ("q", "k", "v", "z", "beta"):
+            sub[key] = inp[key][:, :pos]
+        _, ref, _ = oracle_prefill(sub, heads=heads, nthreads=16)
+        e = rel_err(np64(ck[:, j][:, heads]), ref)
+        print(f"slot {j} (after {pos} tokens): rel err {e:.3e}")
+        assert e <= tol, (j, e)
+
+
 def test_checkpoint_shape_rejected():
     inp = _packed(W.WORKLOADS["varlen_64"], [200, 100], H=2, seed=34)
     bad = torch.zeros((2, 2, 3, 128, 128), device="cuda")  # H = 3, inputs have 2
