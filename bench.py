@@ -1,11 +1,13 @@
 """Benchmark of the KDA core on one MI355X.
 
-One step = one ``kda_chunk_fwd`` call over the prefill_8k workload (B=1,
-T=8192, H=32, d_k=d_v=128, chunk 64, bf16 q/k/v/z/beta, fp32 state) with its
-inputs already resident in HBM; three independent input sets rotate so no
-step reads the previous step's inputs from the 256 MB last-level cache.  The
-decode workload (512 sequences x 32 heads, fp32 state of 1 GiB updated in
-place, 64 steps with fresh inputs) is timed alongside.  Prints one JSON line.
+One step = one ``kda_chunk_fwd`` call over the varlen_64 workload (64 packed
+sequences, lengths U{128..16384}, 530,033 tokens, H=32, d_k=d_v=128, chunk 64,
+bf16 q/k/v/z/beta, per-sequence fp32 initial and final states) with its inputs
+already resident in HBM: the largest prefill configuration that fits one GPU.
+The prefill_8k and prefill_128k configurations, the decode workload (512
+sequences x 32 heads, fp32 state of 1 GiB updated in place, 64 steps with
+fresh inputs), the speculative window and the fused layer are timed alongside.
+Prints one JSON line.
 
 Roofline figures use algorithmic counts per (token, head) at d = 128, C = 64
 (derived from eq. (1) and the chunkwise form of eqs. (3)-(4) of "Kimi K3
@@ -112,17 +114,23 @@ def time_calls(fn, n, stream):
     return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
 
 
-def bench_prefill(steps, warmup, n_sets=3, ckpt_every=0):
-    """prefill_8k timed per call.  ckpt_every > 0 also writes a prefix-state
-    checkpoint every ckpt_every chunks (slots for the whole sequence)."""
-    w = W.WORKLOADS["prefill_8k"]
+def bench_prefill(steps, warmup, n_sets=3, ckpt_every=0, name="prefill_8k", keep_inputs=False):
+    """One kda_chunk_fwd call per step over a prefill workload (fixed-length or
+    packed).  n_sets independent input sets rotate so that no step reads the
+    previous step's inputs from the 256 MB last-level cache (one set is enough
+    once a set is many times that size).  ckpt_every > 0 also writes a
+    prefix-state checkpoint every ckpt_every chunks (slots for the whole
+    sequence)."""
+    w = W.WORKLOADS[name]
     import dataclasses
     sets = []
     for i in range(n_sets):
         inp = W.make_prefill(dataclasses.replace(w, seed=w.seed + 17 * i), device="cuda")
+        cu = inp["cu_seqlens"]
+        N = cu.numel() - 1 if cu is not None else inp["q"].shape[0]
         o = torch.empty_like(inp["v"])
         hT = torch.empty_like(inp["h0"])
-        nws = kda.chunk_fwd_workspace_size(inp["q"], inp["v"])
+        nws = kda.chunk_fwd_workspace_size(inp["q"], inp["v"], cu_seqlens=cu, N=N if cu is not None else None)
         ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
         ck = None
         if ckpt_every > 0:
@@ -135,22 +143,46 @@ def bench_prefill(steps, warmup, n_sets=3, ckpt_every=0):
     def call(i):
         inp, o, hT, ws, ck = sets[i % n_sets]
         kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["z"], inp["beta"], A_log=inp["A_log"],
-                      g_min=inp["g_min"], initial_state=inp["h0"], out=o, final_state=hT,
-                      workspace=ws, stream=stream, checkpoints=ck, checkpoint_every=ckpt_every)
+                      g_min=inp["g_min"], cu_seqlens=inp["cu_seqlens"], initial_state=inp["h0"], out=o,
+                      final_state=hT, workspace=ws, stream=stream, checkpoints=ck, checkpoint_every=ckpt_every)
 
     for i in range(warmup):
         call(i)
     per_call, wall = time_calls(call, steps, stream)
-    B, T, H, Dk = sets[0][0]["q"].shape
-    Dv = sets[0][0]["v"].shape[-1]
-    nbytes, flops = prefill_counts(B * T, H, Dk, Dv, B)
+    inp0 = sets[0][0]
+    tokens = W.n_tokens(inp0)
+    H, Dk = inp0["q"].shape[-2:]
+    Dv = inp0["v"].shape[-1]
+    N = inp0["h0"].shape[0]
+    nbytes, flops = prefill_counts(tokens, H, Dk, Dv, N)
     ms = sum(per_call) / len(per_call)
     n_ck = 0
     if ckpt_every > 0:  # slots strictly inside the sequence are written
-        n_ck = B * H * min(sets[0][4].shape[1], (T - 1) // (64 * ckpt_every))
-    return dict(ms=ms, ms_min=min(per_call), ms_median=statistics.median(per_call), wall_ms=wall, tokens=B * T,
-                bytes=nbytes + 4 * Dk * Dv * n_ck, flops=flops, inputs=sets[0][0], shape=(B, T, H, Dk, Dv),
-                checkpoint_states=n_ck)
+        T = inp0["q"].shape[1]
+        n_ck = N * H * min(sets[0][4].shape[1], (T - 1) // (64 * ckpt_every))
+    out = dict(ms=ms, ms_min=min(per_call), ms_median=statistics.median(per_call), wall_ms=wall, tokens=tokens,
+               sequences=N, bytes=nbytes + 4 * Dk * Dv * n_ck, flops=flops, shape=(tokens, H, Dk, Dv),
+               checkpoint_states=n_ck)
+    if keep_inputs:
+        out["inputs"] = inp0
+    del sets
+    return out
+
+
+def prefill_line(r, kernel, traffic_name):
+    """Throughput, HBM roofline and MFMA-rate figures of one prefill measurement."""
+    sec = r["ms"] / 1e3
+    achieved = r["bytes"] / sec / 1e9
+    tflops = r["flops"] / sec / 1e12
+    return {
+        "ms_per_call": r["ms"], "ms_min": r["ms_min"], "ms_median": r["ms_median"],
+        "tokens": r["tokens"], "sequences": r["sequences"], "tokens_per_s": r["tokens"] / sec,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(traffic_name),
+                     "algorithmic_bytes": r["bytes"]},
+        "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops": r["flops"]},
+    }
 
 
 def bench_decode(warmup_rounds=1):
@@ -176,36 +208,6 @@ def bench_decode(warmup_rounds=1):
     us = 1e3 * sum(per_call) / len(per_call)
     return dict(us=us, us_min=1e3 * min(per_call), us_median=1e3 * statistics.median(per_call), steps=len(steps),
                 N=N, H=H, bytes=nbytes, flops=flops)
-
-
-def bench_prefill_config(name, steps=5, warmup=2):
-    """One kda_chunk_fwd call over a whole prefill workload (fixed-length or packed)."""
-    w = W.WORKLOADS[name]
-    inp = W.make_prefill(w, device="cuda")
-    cu = inp["cu_seqlens"]
-    N = cu.numel() - 1 if cu is not None else inp["q"].shape[0]
-    o = torch.empty_like(inp["v"])
-    hT = torch.empty_like(inp["h0"])
-    nws = kda.chunk_fwd_workspace_size(inp["q"], inp["v"], cu_seqlens=cu, N=N if cu is not None else None)
-    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def call(i):
-        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["z"], inp["beta"], A_log=inp["A_log"], g_min=inp["g_min"],
-                      cu_seqlens=cu, initial_state=inp["h0"], out=o, final_state=hT, workspace=ws, stream=stream)
-
-    for i in range(warmup):
-        call(i)
-    per_call, _ = time_calls(call, steps, stream)
-    tokens = W.n_tokens(inp)
-    H, Dk = inp["q"].shape[-2:]
-    Dv = inp["v"].shape[-1]
-    nbytes, flops = prefill_counts(tokens, H, Dk, Dv, N)
-    ms = sum(per_call) / len(per_call)
-    del inp, o, hT, ws
-    return {"ms_per_call": ms, "ms_min": min(per_call), "tokens": tokens, "sequences": N,
-            "tokens_per_s": tokens / (ms / 1e3), "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
 
 
 def spec_counts(N, H, Dk, Dv, n_replayed, T_new, elem=2):
@@ -401,35 +403,43 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
-def cpu_baseline(inp, max_threads=16, min_seconds=10.0):
-    """The fp64 oracle on the host cores, over the full prefill_8k input set,
-    repeated until at least min_seconds have been timed (the mean over all runs
-    is reported), and on one thread over the first 2 heads.  Reported baseline
-    only."""
+def cpu_baseline(inp, max_threads=16, min_seconds=10.0, max_seconds=30.0):
+    """The fp64 oracle on the host cores over the headline workload, streamed
+    one head at a time (every packed sequence of that head in one oracle call,
+    OpenMP over the sequences), heads taken in order until at least
+    min_seconds of oracle time have accumulated or every head is done, and
+    stopped early once max_seconds would be passed.  Only the oracle calls are
+    timed (not the copies to the host).  Reported as tokens/s of the whole
+    workload: (token-heads per second) / H.  Reported baseline only."""
     import oracle
-    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()[0]
-    q, k, v, z, b = (f64(inp[x]) for x in ("q", "k", "v", "z", "beta"))
-    h0 = inp["h0"].detach().to("cpu", torch.float64).numpy()
-    A = inp["A_log"].detach().to("cpu", torch.float64).numpy()
+    cu = inp["cu_seqlens"]
+    H = inp["q"].shape[-2]
+    flat = lambda t: t.reshape((-1,) + tuple(t.shape[-2:])) if t.dim() == 4 else t
+    q, k, v, z = (flat(inp[x]) for x in ("q", "k", "v", "z"))
+    b = inp["beta"].reshape(-1, H)
+    T = q.shape[0]
+    cu_np = (cu.to("cpu", torch.int64).numpy() if cu is not None
+             else (torch.arange(inp["q"].shape[0] + 1, dtype=torch.int64) * inp["q"].shape[1]).numpy())
+    N = cu_np.size - 1
     threads = min(max_threads, os.cpu_count() or 1)
-    best, used, runs, total = None, threads, 0, 0.0
-    while runs < 2 or total < min_seconds:
+    host = lambda t: t.detach().to("cpu", torch.float64).numpy()
+    total, used, heads = 0.0, threads, 0
+    for h in range(H):
+        sl = slice(h, h + 1)
+        args = [host(x[:, sl]) for x in (q, k, v, z)] + [host(b[:, sl])]
+        h0 = host(inp["h0"][:, sl])
+        A = host(inp["A_log"][sl])
         t0 = time.perf_counter()
-        _, _, used = oracle.forward(q, k, v, z, b, h0=h0, A_log=A, g_min=inp["g_min"], nthreads=threads,
+        _, _, used = oracle.forward(*args, cu_seqlens=cu_np, h0=h0, A_log=A, g_min=inp["g_min"], nthreads=threads,
                                     return_threads=True)
         dt = time.perf_counter() - t0
-        best = dt if best is None else min(best, dt)
-        runs, total = runs + 1, total + dt
-    T, H = q.shape[0], q.shape[1]
-    h1 = 2  # one-thread run: 2 of the heads, scaled to the full workload
-    t0 = time.perf_counter()
-    oracle.forward(q[:, :h1].copy(), k[:, :h1].copy(), v[:, :h1].copy(), z[:, :h1].copy(), b[:, :h1].copy(),
-                   h0=h0[:, :h1].copy(), A_log=A[:h1].copy(), g_min=inp["g_min"], nthreads=1)
-    one = (time.perf_counter() - t0) * H / h1
-    return {"value": T * runs / total, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
-            "sample": f"full prefill_8k workload ({T} tokens x {H} heads), fp64, {runs} runs in {total:.1f} s "
-                      f"(mean; fastest run {best:.3f} s)",
-            "one_thread_tokens_per_s": T / one, "host_cpus": os.cpu_count(), "host_cpu_model": cpu_model()}
+        total, heads = total + dt, heads + 1
+        if total >= min_seconds or total * (heads + 1) / heads > max_seconds:
+            break
+    return {"value": T * heads / H / total, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{heads} of {H} heads of the headline workload ({N} sequences, {T} tokens each head), "
+                      f"fp64, {total:.1f} s of oracle time, scaled to all {H} heads",
+            "host_cpus": os.cpu_count(), "host_cpu_model": cpu_model()}
 
 
 def measured_peaks():
@@ -448,20 +458,26 @@ def measured_peaks():
             "copy_1GiB_read_plus_write_gbs": cp["GBps_read_plus_write"]}
 
 
+PREFILL_KERNELS = "kda_chunk_fwd (intra_chunk_kernel + chain_kernel; chunk_table_kernel for packed input)"
+HEADLINE = "varlen_64"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured GEMM / copy reference peaks")
     ap.add_argument("--no-spec", action="store_true", help="skip the speculative-decoding replay measurement")
-    ap.add_argument("--no-other", action="store_true", help="skip the prefill_128k and varlen_64 measurements")
+    ap.add_argument("--no-other", action="store_true", help="skip the prefill_8k and prefill_128k measurements")
     ap.add_argument("--no-layer", action="store_true", help="skip the fused-layer (prologue / epilogue) measurements")
-    ap.add_argument("--mode", choices=["all", "prefill", "decode", "spec", "layer", "copy"], default="all",
-                    help="prefill/decode/copy run one part only (for profiler runs); the JSON line "
-                         "of the benchmark contract is printed in mode 'all'")
+    ap.add_argument("--mode", choices=["all", "varlen", "prefill", "prefill128k", "decode", "spec", "layer", "copy"],
+                    default="all",
+                    help="every mode but 'all' runs one part only (for profiler runs: varlen = the headline "
+                         "varlen_64 call, prefill = prefill_8k); the JSON line of the benchmark contract is "
+                         "printed in mode 'all'")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (run with --gpus 1)",
@@ -487,49 +503,59 @@ def main():
         ls = bench_layer_spec()
         print(json.dumps({"prefill_ms": lp["ms"], "decode_us": ld["us"], "spec_us": ls["us"]}))
         return
-
-    pf = bench_prefill(args.steps, args.warmup)
-    if args.mode == "prefill":
-        print(json.dumps({"ms": pf["ms"], "ms_min": pf["ms_min"], "tokens_per_s": pf["tokens"] / (pf["ms"] / 1e3)}))
+    if args.mode in ("varlen", "prefill", "prefill128k"):
+        name = {"varlen": "varlen_64", "prefill": "prefill_8k", "prefill128k": "prefill_128k"}[args.mode]
+        r = bench_prefill(args.steps, args.warmup, n_sets=3 if name == "prefill_8k" else 1, name=name)
+        print(json.dumps({"workload": name, "ms": r["ms"], "ms_min": r["ms_min"],
+                          "tokens_per_s": r["tokens"] / (r["ms"] / 1e3)}))
         return
-    sec = pf["ms"] / 1e3
-    achieved = pf["bytes"] / sec / 1e9
-    tflops = pf["flops"] / sec / 1e12
-    B, T, H, Dk, Dv = pf["shape"]
+
+    # headline: the largest prefill configuration (530,033 packed tokens; one input set of ~17 GB
+    # is far larger than the 256 MB last-level cache, so no rotation is needed)
+    hv = bench_prefill(args.steps, args.warmup, n_sets=1, name=HEADLINE, keep_inputs=not args.no_cpu_baseline)
+    line = prefill_line(hv, PREFILL_KERNELS, "varlen")
+    tokens, H, Dk, Dv = hv["shape"]
     result = {
         "metric": METRIC,
-        "value": pf["tokens"] / sec,
+        "value": line["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": pf["ms"],
+        "ms_per_step": hv["ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"prefill_8k: B={B} T={T} H={H} d_k={Dk} d_v={Dv} chunk=64, "
-                               "bf16 q/k/v/z/beta, fp32 initial+final state, eq.(5) gate in-kernel",
-                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd (intra_chunk_kernel + chain_kernel)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic("prefill"),
-                     "algorithmic_bytes": pf["bytes"]},
-        "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops": pf["flops"]},
-        "prefill_ms_min": pf["ms_min"],
-        "prefill_ms_median": pf["ms_median"],
-        "prefill_wall_ms": pf["wall_ms"],
+        "config": {"workload": f"varlen_64: {hv['sequences']} packed sequences (cu_seqlens), lengths U{{128..16384}}, "
+                               f"{tokens} tokens, H={H} d_k={Dk} d_v={Dv} chunk=64, bf16 q/k/v/z/beta, per-sequence "
+                               "fp32 initial+final states, eq.(5) gate in-kernel",
+                   "global_batch": hv["sequences"], "seq_len": tokens, "parallelism": "none (1 GPU)"},
+        "roofline": line["roofline"],
+        "mfma": line["mfma"],
+        "ms_min": hv["ms_min"],
+        "ms_median": hv["ms_median"],
+        "wall_ms": hv["wall_ms"],
     }
-    ck = bench_prefill(args.steps, args.warmup, ckpt_every=8)
-    result["prefill_with_checkpoints"] = {
-        "workload": "prefill_8k with a prefix-state checkpoint every 8 chunks (512 tokens), fp32 slots",
-        "ms_per_step": ck["ms"], "ms_median": ck["ms_median"], "tokens_per_s": ck["tokens"] / (ck["ms"] / 1e3),
-        "checkpoint_states_written": ck["checkpoint_states"],
-        "hbm_GBps": ck["bytes"] / (ck["ms"] / 1e3) / 1e9, "algorithmic_bytes": ck["bytes"],
-        "overhead_vs_plain": ck["ms"] / pf["ms"] - 1.0,
-    }
+    inputs = hv.pop("inputs", None)
+    pf = None
+    if not args.no_other:
+        pf = bench_prefill(args.steps, args.warmup, n_sets=3, name="prefill_8k")
+        result["prefill_8k"] = {"workload": "prefill_8k: B=1 T=8192 H=32 d=128 chunk=64, bf16, fp32 initial+final "
+                                            "state; three input sets rotate", **prefill_line(pf, PREFILL_KERNELS, "prefill")}
+        ck = bench_prefill(args.steps, args.warmup, ckpt_every=8, name="prefill_8k")
+        result["prefill_with_checkpoints"] = {
+            "workload": "prefill_8k with a prefix-state checkpoint every 8 chunks (512 tokens), fp32 slots",
+            "ms_per_step": ck["ms"], "ms_median": ck["ms_median"], "tokens_per_s": ck["tokens"] / (ck["ms"] / 1e3),
+            "checkpoint_states_written": ck["checkpoint_states"],
+            "hbm_GBps": ck["bytes"] / (ck["ms"] / 1e3) / 1e9, "algorithmic_bytes": ck["bytes"],
+            "overhead_vs_plain": ck["ms"] / pf["ms"] - 1.0,
+        }
+        p128 = bench_prefill(max(3, args.steps // 4), 1, n_sets=1, name="prefill_128k")
+        result["prefill_128k"] = {"workload": "prefill_128k: B=1 T=131072 H=32 d=128, 5% of decay channels forced "
+                                              "each way", **prefill_line(p128, PREFILL_KERNELS, "prefill128k")}
+        torch.cuda.empty_cache()
     if not args.no_decode:
         dc = bench_decode()
         gbs = dc["bytes"] / (dc["us"] / 1e6) / 1e9
@@ -574,9 +600,9 @@ def main():
                     "(RMSNorm, Sigmoid output gate) fused around the recurrence; dense projections not included",
             "prefill": {"workload": f"prefill_8k shapes (B={B_} T={T_} H={H_} d={Dk_}) from pre-convolution "
                                     "projections, bf16", "ms_per_call": lp["ms"], "ms_median": lp["ms_median"],
-                        "tokens_per_s": lp["tokens"] / (lp["ms"] / 1e3), "vs_core_call": lp["ms"] / pf["ms"],
-                        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd with fusion (prologue_kernel + "
-                                     "intra_chunk_kernel + chain_kernel + gate_norm_kernel)", "achieved": lp_gbs,
+                        "tokens_per_s": lp["tokens"] / (lp["ms"] / 1e3),
+                        "vs_core_call": lp["ms"] / pf["ms"] if pf else None,
+                        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd with fusion", "achieved": lp_gbs,
                                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lp_gbs / HBM_PEAK_GBS,
                                      "traffic": profiled_traffic("layer_prefill"), "algorithmic_bytes": lp["bytes"]}},
             "decode": {"workload": f"decode_512 shapes (N={ld['N']} x 1 token, H={ld['H']}, d=128), fp32 state and "
@@ -596,22 +622,16 @@ def main():
                                   "traffic": profiled_traffic("layer_spec"), "algorithmic_bytes": ls["bytes"]}},
         }
         torch.cuda.empty_cache()
-    if not args.no_other:
-        result["other_prefill"] = {
-            "prefill_128k: B=1 T=131072 H=32 d=128, 5% of decay channels forced each way": bench_prefill_config("prefill_128k"),
-            "varlen_64: 64 packed sequences, lengths U{128..16384}, 530,033 tokens, H=32 d=128": bench_prefill_config("varlen_64"),
-        }
-        torch.cuda.empty_cache()
     if not args.no_peaks:
         pk = measured_peaks()
         result["measured_peaks"] = pk
-        result["roofline"]["frac_of_measured_copy"] = achieved / pk["copy_1GiB_read_plus_write_gbs"]
-        result["mfma"]["frac_of_measured_gemm"] = tflops / pk["bf16_gemm_8192_tflops"]
+        result["roofline"]["frac_of_measured_copy"] = result["roofline"]["achieved"] / pk["copy_1GiB_read_plus_write_gbs"]
+        result["mfma"]["frac_of_measured_gemm"] = result["mfma"]["achieved"] / pk["bf16_gemm_8192_tflops"]
         if "decode" in result:
             d = result["decode"]["roofline"]
             d["frac_of_measured_copy"] = d["achieved"] / pk["copy_1GiB_read_plus_write_gbs"]
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(pf["inputs"])
+    if not args.no_cpu_baseline and inputs is not None:
+        result["cpu_baseline"] = cpu_baseline(inputs)
     print(json.dumps(result))
 
 

@@ -1112,7 +1112,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrefillParams p)
         const int rb = (nv - 1) * p.H * EL + EL;
         const __amdgpu_buffer_rsrc_t ib = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.beta + r0), 0, rb, 0x00020000);
         const __amdgpu_buffer_rsrc_t ob = __builtin_amdgcn_make_buffer_rsrc((void *)((T *)p.pro_b + r0), 0, rb, 0x00020000);
-        const int off = (l < TW ? l : 0x4000000) * p.H * EL;  // lanes past the wave's tokens read and write nothing
+        const int off = l < TW ? l * p.H * EL : 0x40000000;  // lanes past the wave's tokens: past the record count, nothing read or written
         const T b = buf_load<T>(ib, off);
         buf_store<T>(ob, off, from_f<T>(1.f / (1.f + __expf(-to_f<T>(b)))));
     }

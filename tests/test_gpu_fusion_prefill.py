@@ -4,10 +4,14 @@
 Reference: oracle.layer (fp64).  States and the recurrence output o~ within
 the dtype's bound; convolution states (copies of input values) bit for bit.
 The epilogue divides each (token, head) row by its own RMS, which scales a
-small row's absolute error up with it, so with bf16 operands its output is
-checked in two parts: o~ (the same call without the epilogue) against the
-oracle within the bound, and the fused output against the fp64 epilogue of
-that o~ within EPI_TOL (bf16 output rounding and the fp32 sigmoid / rsqrt).
+small row's absolute error up with it, so with bf16 operands the fused output
+y is held end to end against the oracle's y (its own epilogue of its own o~)
+within a per-element bound derived from the core's bound and the row's RMS
+(kda_testutil.epilogue_bound, pinned on the CPU in test_epilogue_bound.py).
+In addition, o~ (the same call without the epilogue) is held against the
+oracle within the core bound, and the fused output against the fp64
+epilogue of that o~ within EPI_TOL (bf16 output rounding and the fp32
+sigmoid / rsqrt).
 Cases span several chunks with a ragged tail, packed sequences shorter than
 the filter, prefix checkpoints, and a prefill handing its states to fused
 decode steps."""
@@ -19,7 +23,7 @@ import torch
 
 import oracle.layer as L
 import workloads as W
-from kda_testutil import TOL, np64, rel_err
+from kda_testutil import TOL, check_epilogue_end_to_end, np64, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -68,10 +72,14 @@ def _ref(d, pro, epi, cu=None, conv_state=None, h0=None):
 
 def _check_output(y, o_plain, d, pro, epi, tol, **ref_kw):
     """y: the call's output; o_plain: the same call's output without the
-    epilogue.  fp32: y end to end; bf16: o_plain against the oracle and y
-    against the fp64 epilogue of o_plain (see the module docstring)."""
+    epilogue.  fp32: y end to end within the core bound; bf16: y end to end
+    within the derived per-element bound, plus o_plain against the oracle and
+    y against the fp64 epilogue of o_plain (see the module docstring)."""
     if epi and tol > TOL[torch.float32]:
         o_ref, _, _ = _ref(d, pro, False, **ref_kw)
+        ratio, e_y = check_epilogue_end_to_end(np64(y), o_ref, np64(d["gate"]), np64(d["o_norm_weight"]), O_EPS, tol)
+        print(f"fused y end to end: worst |dy| / bound {ratio:.3f}, whole-tensor rel err {e_y:.3e}")
+        assert ratio <= 1.0, ratio
         assert rel_err(np64(o_plain), o_ref) <= tol
         assert rel_err(np64(y), L.epilogue(np64(o_plain), np64(d["gate"]), np64(d["o_norm_weight"]), O_EPS)) <= EPI_TOL
     else:
