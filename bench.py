@@ -458,6 +458,11 @@ def measured_peaks():
             "copy_1GiB_read_plus_write_gbs": cp["GBps_read_plus_write"]}
 
 
+def log(msg):
+    """Progress line on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 PREFILL_KERNELS = "kda_chunk_fwd (intra_chunk_kernel + chain_kernel; chunk_table_kernel for packed input)"
 HEADLINE = "varlen_64"
 
@@ -514,6 +519,7 @@ def main():
     # is far larger than the 256 MB last-level cache, so no rotation is needed)
     hv = bench_prefill(args.steps, args.warmup, n_sets=1, name=HEADLINE, keep_inputs=not args.no_cpu_baseline)
     line = prefill_line(hv, PREFILL_KERNELS, "varlen")
+    log(f"{HEADLINE}: {hv['ms']:.3f} ms per call")
     tokens, H, Dk, Dv = hv["shape"]
     result = {
         "metric": METRIC,
@@ -552,12 +558,15 @@ def main():
             "hbm_GBps": ck["bytes"] / (ck["ms"] / 1e3) / 1e9, "algorithmic_bytes": ck["bytes"],
             "overhead_vs_plain": ck["ms"] / pf["ms"] - 1.0,
         }
+        log(f"prefill_8k: {pf['ms'] * 1e3:.1f} us per call, with checkpoints {ck['ms'] * 1e3:.1f} us")
         p128 = bench_prefill(max(3, args.steps // 4), 1, n_sets=1, name="prefill_128k")
+        log(f"prefill_128k: {p128['ms']:.3f} ms per call")
         result["prefill_128k"] = {"workload": "prefill_128k: B=1 T=131072 H=32 d=128, 5% of decay channels forced "
                                               "each way", **prefill_line(p128, PREFILL_KERNELS, "prefill128k")}
         torch.cuda.empty_cache()
     if not args.no_decode:
         dc = bench_decode()
+        log(f"decode_512: {dc['us']:.1f} us per step")
         gbs = dc["bytes"] / (dc["us"] / 1e6) / 1e9
         result["decode"] = {
             "workload": f"decode_512: N={dc['N']} x 1 token, H={dc['H']}, d=128, fp32 state 1 GiB in place, "
@@ -575,6 +584,7 @@ def main():
         for tn in (1, 2, 4, 8):
             r = bench_spec(T_new=tn, calls=8)
             window[str(tn)] = round(r["us"], 1)
+        log(f"decode_512_spec: {sp['us']:.1f} us per call; by new window {window}")
         result["spec_decode"] = {
             "workload": f"decode_512_spec: N={sp['N']}, H={sp['H']}, d=128, cached drafts {sp['T_replay']} "
                         f"(mean {sp['mean_replayed']:.2f} accepted and replayed), new window {sp['T_new']} "
@@ -594,6 +604,7 @@ def main():
         lp_gbs = lp["bytes"] / (lp["ms"] / 1e3) / 1e9
         ld_gbs = ld["bytes"] / (ld["us"] / 1e6) / 1e9
         ls_gbs = ls["bytes"] / (ls["us"] / 1e6) / 1e9
+        log(f"layer: prefill {lp['ms'] * 1e3:.1f} us, decode {ld['us']:.1f} us, spec {ls['us']:.1f} us")
         B_, T_, H_, Dk_, Dv_ = lp["shape"]
         result["layer"] = {
             "what": "eq. (2) prologue (ShortConv width 4, Swish, L2Norm, Sigmoid beta) and eq. (6) epilogue "
@@ -624,6 +635,7 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_peaks:
         pk = measured_peaks()
+        log(f"measured peaks: {pk}")
         result["measured_peaks"] = pk
         result["roofline"]["frac_of_measured_copy"] = result["roofline"]["achieved"] / pk["copy_1GiB_read_plus_write_gbs"]
         result["mfma"]["frac_of_measured_gemm"] = result["mfma"]["achieved"] / pk["bf16_gemm_8192_tflops"]
@@ -631,7 +643,9 @@ def main():
             d = result["decode"]["roofline"]
             d["frac_of_measured_copy"] = d["achieved"] / pk["copy_1GiB_read_plus_write_gbs"]
     if not args.no_cpu_baseline and inputs is not None:
+        log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(inputs)
+        log(f"cpu baseline: {result['cpu_baseline']['value']:.0f} tokens/s on {result['cpu_baseline']['cores']} threads")
     print(json.dumps(result))
 
 

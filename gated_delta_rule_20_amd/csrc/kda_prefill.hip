@@ -47,15 +47,18 @@ namespace kda {
 
 // -----------------------------------------------------------------------------
 // Per (head, chunk) workspace block written by intra_chunk_kernel and read by
-// chain_kernel.  Element type T except gamma (fp32).  "wave w" is the chain
-// kernel's wave index: token rows 16w..16w+15 of the chunk, and state rows
+// the chain kernels.  Element type T except gamma (fp32).  "wave w" is the
+// slice chain's wave index: token rows 16w..16w+15 of the chunk, and state rows
 // 16*RT*w .. 16*RT*(w+1)-1.  All fragments use kmap() along k.
 //   Wn  [4 waves][KS][64 lanes][8]  A-operand fragments of -W    (rows tokens, k channels)
 //   Qp  [4 waves][KS][64][8]        operand fragments of scale*Q*Gamma (rows tokens, k channels)
 //   Kt  [4 waves][RT][2][64][8]     A-operand fragments of (K*gamma^C/Gamma)^T (rows channels, k tokens)
 //   A   [4 waves][2][64][8]         A-operand fragments of A     (rows tokens, k tokens)
-//   U   [NS][4 waves][64][4]        accumulator quads of U
 //   gamma [DK] float                gamma^C = exp(lam at the chunk's last token)
+//   U   [NS][4 waves][64][4]        accumulator quads of U
+// Everything up to U is what every wave of the wide chain reads; with U right
+// behind it the block is one contiguous run that the wide chain copies into
+// LDS in 1 KiB pieces (the block is a whole number of them).
 // -----------------------------------------------------------------------------
 template <typename T, int DK, int DV> struct Block {
     static constexpr int KS = DK / 32;
@@ -65,10 +68,13 @@ template <typename T, int DK, int DV> struct Block {
     static constexpr size_t Q_OFF = W_OFF + (size_t)4 * KS * 512;
     static constexpr size_t KT_OFF = Q_OFF + (size_t)4 * KS * 512;
     static constexpr size_t A_OFF = KT_OFF + (size_t)4 * RT * 2 * 512;
-    static constexpr size_t U_OFF = A_OFF + (size_t)4 * 2 * 512;
-    static constexpr size_t T_ELEMS = U_OFF + (size_t)NS * 4 * 256;
-    static constexpr size_t GAMMA_BYTE = T_ELEMS * sizeof(T);
-    static constexpr size_t BYTES = (GAMMA_BYTE + DK * sizeof(float) + 255) / 256 * 256;
+    static constexpr size_t GAMMA_BYTE = (A_OFF + (size_t)4 * 2 * 512) * sizeof(T);
+    static constexpr size_t STAGE_BYTES = GAMMA_BYTE + DK * sizeof(float);
+    static constexpr size_t U_BYTE = STAGE_BYTES;
+    static constexpr size_t U_OFF = U_BYTE / sizeof(T);
+    static constexpr size_t U_BYTES = (size_t)NS * 4 * 256 * sizeof(T);
+    static constexpr size_t BYTES = (U_BYTE + U_BYTES + 1023) / 1024 * 1024;
+    static_assert(U_BYTE % 16 == 0, "U quads must stay 16-byte aligned");
 };
 
 size_t block_bytes(int bf16_, int Dk, int Dv)
@@ -266,7 +272,7 @@ template <typename V> __device__ __forceinline__ V buf_load(__amdgpu_buffer_rsrc
         return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, 0));
 }
 
-// Raw buffer store of a 2-, 4- or 8-byte vector; offsets at or past the
+// Raw buffer store of a 2-, 4-, 8- or 16-byte vector; offsets at or past the
 // descriptor's record count are dropped.
 template <typename V> __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, int voff, V v)
 {
@@ -274,10 +280,16 @@ template <typename V> __device__ __forceinline__ void buf_store(__amdgpu_buffer_
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), rs, voff, 0, 0);
     else if constexpr (sizeof(V) == 4)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff, 0, 0);
-    else
+    else if constexpr (sizeof(V) == 8)
     {
         typedef unsigned u32x2 __attribute__((vector_size(8)));
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, voff, 0, 0);
+    }
+    else
+    {
+        static_assert(sizeof(V) == 16, "2, 4, 8 or 16 bytes");
+        typedef unsigned u32x4 __attribute__((vector_size(16)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff, 0, 0);
     }
 }
 
@@ -939,6 +951,237 @@ __global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
 }
 
 // -----------------------------------------------------------------------------
+// Wide chain: one workgroup of four waves per (sequence, head), for inputs with
+// many (sequence, head) pairs, where throughput, not the length of one chain,
+// sets the time.  Wave w owns CT = d_v / 64 column tiles (16 columns each) of S
+// with all d_k rows, as fp32 MFMA accumulators: lane (x, g) of tile (R, c)
+// holds S[16R + 4g + i][col(c) + x].  With the shared k-map those registers,
+// rounded to T, are exactly the operand fragments of the products that
+// contract over d_k (B of W S, A of S^T (Q+)^T), and the accumulators of
+// V~ = U - W S are exactly those of the products that contract over tokens
+// (B of K~^T V~, A of V~^T A^T): the recurrence runs inside each wave, with no
+// exchange.  The chunk's whole block (operands every wave reads, then U) is
+// copied into LDS by direct global->LDS loads, one chunk ahead into the other
+// of two buffers (two LDS arrays, so the compiler can tell a copy in flight
+// into one from the reads of the other); each wave issues its share of the
+// copies in four parts spread over the chunk's products, so that no wave
+// stalls on a burst of memory requests.  Per (chunk, head) one compute unit
+// does the work that the slice chain spreads over eight, at about three times
+// the time per chunk: the slice chain is for long chains with few pairs.
+// -----------------------------------------------------------------------------
+template <typename T, int DK, int DV> struct WideShape {
+    using BL = Block<T, DK, DV>;
+    static constexpr int NLD = (int)((BL::STAGE_BYTES + 1023) / 1024);  // pieces of the shared operands
+    // U goes through LDS with the operands when both buffers fit (every bf16
+    // shape); otherwise (fp32) the waves read it from the block.
+    static constexpr bool ULDS = 2 * BL::BYTES <= 160 * 1024;
+    static constexpr int NPC = ULDS ? (int)(BL::BYTES / 1024) : NLD;   // pieces copied per chunk
+};
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void chain_wide_kernel(PrefillParams p)
+{
+    using BL = Block<T, DK, DV>;
+    using WS = WideShape<T, DK, DV>;
+    constexpr int KS = DK / 32, NR = DK / 16, CT = DV / 64;
+    constexpr int FB = (int)sizeof(frag_t<T>), QB = (int)sizeof(quad_t<T>), EL = (int)sizeof(T);
+    constexpr int NPC = WS::NPC;
+    constexpr bool ULDS = WS::ULDS;
+    constexpr int PER = (NPC + 3) / 4, PART = (PER + 3) / 4;  // pieces per wave, per part
+    __shared__ __align__(16) char sA[NPC * 1024];
+    __shared__ __align__(16) char sB[NPC * 1024];
+
+    const int pair = blockIdx.x;
+    if (pair >= p.N * p.H) return;
+    const int srank = pair / p.H, h = pair - srank * p.H;
+    int s, tok0, len, chunk0, nch;
+    if (p.varlen) {
+        s = p.order[srank];
+        tok0 = p.cu[s];
+        len = p.cu[s + 1] - tok0;
+        chunk0 = p.chunk_off[s];
+        nch = p.chunk_off[s + 1] - chunk0;
+    } else {
+        s = srank;
+        tok0 = s * p.T;
+        len = p.T;
+        nch = (p.T + CHUNK - 1) / CHUNK;
+        chunk0 = s * nch;
+    }
+    const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int l = t & 63, g = l >> 4, x = l & 15;
+    const int ct0 = w * CT;  // first column tile of this wave
+    const size_t sbase = ((size_t)s * p.H + h) * DK * DV;
+    const char *blk0 = p.blocks + ((size_t)h * p.n_chunks_cap + chunk0) * BL::BYTES;
+
+    f32x4 S[NR][CT];
+#pragma unroll
+    for (int R = 0; R < NR; ++R)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) S[R][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.h0) {
+#pragma unroll
+        for (int R = 0; R < NR; ++R)
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[R][c][i] = p.h0[sbase + (size_t)(16 * R + 4 * g + i) * DV + 16 * (ct0 + c) + x];
+    }
+
+    // Part `part` of this wave's copies of chunk lc into buf: pieces w + 4 i for
+    // i in [PART part, PART (part + 1)).
+    auto stage = [&](char *buf, int lc, int part) {
+        const char *b = blk0 + (size_t)lc * BL::BYTES + l * 16;
+#pragma unroll
+        for (int i = PART * part; i < PART * (part + 1); ++i) {
+            const int j = w + 4 * i;
+            if (j < NPC)
+                __builtin_amdgcn_global_load_lds((const void *)(b + j * 1024),
+                                                 (__attribute__((address_space(3))) void *)(buf + j * 1024), 16, 0, 0);
+        }
+    };
+    auto frag = [&](const char *buf, size_t off_elems, int piece) {
+        return *reinterpret_cast<const frag_t<T> *>(buf + off_elems * sizeof(T) + (size_t)piece * 64 * FB + l * FB);
+    };
+    const int rowb = p.H * DV * EL;  // bytes between consecutive tokens of o
+    T *o = (T *)p.o;
+
+    auto step = [&](const char *buf, char *nbuf, int lc) {
+        const bool more = lc + 1 < nch;
+        if (more) stage(nbuf, lc + 1, 0);
+        frag_t<T> Sf[KS][CT];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Sf[ks][c][e] = from_f<T>(S[2 * ks][c][e]);
+                    Sf[ks][c][4 + e] = from_f<T>(S[2 * ks + 1][c][e]);
+                }
+        // V~ = U + (-W) S
+        f32x4 V[4][CT];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                const size_t uo = BL::U_BYTE + (size_t)((ct0 + c) * 4 + m) * 64 * QB + l * QB;
+                V[m][c] = quad_to_f<T>(*reinterpret_cast<const quad_t<T> *>(ULDS ? buf + uo : blk0 + (size_t)lc * BL::BYTES + uo));
+            }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const frag_t<T> wf = frag(buf, BL::W_OFF, m * KS + ks);
+#pragma unroll
+                for (int c = 0; c < CT; ++c) V[m][c] = mma(wf, Sf[ks][c], V[m][c]);
+            }
+        if (more) stage(nbuf, lc + 1, 1);
+        // O^T = S^T (Q+)^T + V~^T A^T (rows columns, columns tokens)
+        f32x4 O[CT][4];
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) O[c][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const frag_t<T> qf = frag(buf, BL::Q_OFF, m * KS + ks);
+#pragma unroll
+                for (int c = 0; c < CT; ++c) O[c][m] = mma(Sf[ks][c], qf, O[c][m]);
+            }
+        if (more) stage(nbuf, lc + 1, 2);
+        frag_t<T> Vf[2][CT];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Vf[ks][c][e] = from_f<T>(V[2 * ks][c][e]);
+                    Vf[ks][c][4 + e] = from_f<T>(V[2 * ks + 1][c][e]);
+                }
+        // S <- Diag(gamma^C) S + (K gamma^C / Gamma)^T V~
+#pragma unroll
+        for (int R = 0; R < NR; ++R) {
+            const f32x4 gam = *reinterpret_cast<const f32x4 *>(buf + BL::GAMMA_BYTE + (16 * R + 4 * g) * 4);
+#pragma unroll
+            for (int c = 0; c < CT; ++c) S[R][c] *= gam;
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int R = 0; R < NR; ++R) {
+                const frag_t<T> kf = frag(buf, BL::KT_OFF, R * 2 + ks);
+#pragma unroll
+                for (int c = 0; c < CT; ++c) S[R][c] = mma(kf, Vf[ks][c], S[R][c]);
+            }
+        if (more) stage(nbuf, lc + 1, 3);
+        // + (A V~)^T; A is lower triangular, so token tiles 0 and 1 have one k-step
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int ks = 0; ks <= m / 2; ++ks) {
+                const frag_t<T> af = frag(buf, BL::A_OFF, m * 2 + ks);
+#pragma unroll
+                for (int c = 0; c < CT; ++c) O[c][m] = mma(Vf[ks][c], af, O[c][m]);
+            }
+        // The next chunk's block has landed (this wave's copies; the barrier below
+        // covers the others'), then this chunk's outputs go out, so the wait does
+        // not include their stores.  o goes through a buffer descriptor whose
+        // record count ends at the chunk's last token (no branch per row).
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        const int clen = min(CHUNK, len - lc * CHUNK);
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(o + ((size_t)(tok0 + lc * CHUNK) * p.H + h) * DV), 0, (clen - 1) * rowb + DV * EL, 0x00020000);
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                buf_store<quad_t<T>>(ro, (16 * m + x) * rowb + (16 * (ct0 + c) + 4 * g) * EL, make_quad<T>(O[c][m]));
+        // Prefix-state checkpoint after every ckpt_every-th chunk strictly inside the sequence.
+        if (p.ckpt_every > 0 && (lc + 1) % p.ckpt_every == 0) {
+            const int j = (lc + 1) / p.ckpt_every - 1;
+            if (j < p.ckpt_slots && (lc + 1) * CHUNK < len) {
+                float *cp = p.ckpt + (((size_t)s * p.ckpt_slots + j) * p.H + h) * DK * DV;
+#pragma unroll
+                for (int R = 0; R < NR; ++R)
+#pragma unroll
+                    for (int c = 0; c < CT; ++c)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            cp[(size_t)(16 * R + 4 * g + i) * DV + 16 * (ct0 + c) + x] = S[R][c][i];
+            }
+        }
+        __builtin_amdgcn_s_barrier();
+    };
+
+    if (nch > 0) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) stage(sA, 0, part);
+    }
+    // Nothing loaded before the chunk loop stays in flight into it (the first
+    // chunk's copies included), so no wait merged into the loop reaches back.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    for (int lc = 0; lc < nch; lc += 2) {
+        step(sA, sB, lc);
+        if (lc + 1 < nch) step(sB, sA, lc + 1);
+    }
+    if (p.hT) {
+#pragma unroll
+        for (int R = 0; R < NR; ++R)
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    p.hT[sbase + (size_t)(16 * R + 4 * g + i) * DV + 16 * (ct0 + c) + x] = S[R][c][i];
+    }
+}
+
+// -----------------------------------------------------------------------------
 // Layer prologue (eq. (2)) as a pass of its own ahead of the intra-chunk stage.
 // (Folded into the intra-chunk kernel's elementwise phase it pushed that kernel
 // past its register budget: spills on the prefetched inputs serialised their
@@ -1183,6 +1426,12 @@ __global__ __launch_bounds__(256) void empty_conv_state_kernel(const PrefillPara
         ((T *)p.f.conv_state_out)[base + e] = p.f.conv_state ? ((const T *)p.f.conv_state)[base + e] : from_f<T>(0.f);
 }
 
+// With this many (sequence, head) pairs or more the chain runs on the wide
+// kernel (one compute unit per pair, about 2.7 times less work per chunk than
+// the slice kernel's eight, each chunk about 3 times slower); below it the
+// slice kernel's shorter time per chunk wins.
+constexpr long WIDE_CHAIN_PAIRS = 128;
+
 // -----------------------------------------------------------------------------
 // Persistent grid of the intra-chunk stage: one workgroup per compute unit
 // (its LDS footprint allows one), queried once from the device.
@@ -1227,8 +1476,12 @@ static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
             hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, false>), dim3(grid), dim3(64 * IWAVES), smem, st, pi);
     }
     const long npairs = (long)p.N * p.H;
-    const unsigned grid = (unsigned)(((npairs + 7) / 8) * 8 * (DV / 16));
-    if (grid > 0) hipLaunchKernelGGL((chain_kernel<T, DK, DV>), dim3(grid), dim3(512), 0, st, p);
+    if (npairs >= WIDE_CHAIN_PAIRS) {
+        hipLaunchKernelGGL((chain_wide_kernel<T, DK, DV>), dim3((unsigned)npairs), dim3(256), 0, st, p);
+    } else {
+        const unsigned grid = (unsigned)(((npairs + 7) / 8) * 8 * (DV / 16));
+        if (grid > 0) hipLaunchKernelGGL((chain_kernel<T, DK, DV>), dim3(grid), dim3(512), 0, st, p);
+    }
     const long rows = (long)(p.varlen ? p.T : (long)p.N * p.T) * p.H;
     if (p.f.gate && rows > 0) {
         constexpr int RPB = 4 * (64 / (DV / (16 / (int)sizeof(T))));  // rows per 256-thread workgroup
