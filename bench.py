@@ -463,7 +463,8 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-PREFILL_KERNELS = "kda_chunk_fwd (intra_chunk_kernel + chain_kernel; chunk_table_kernel for packed input)"
+PREFILL_KERNELS = ("kda_chunk_fwd (intra_chunk_kernel + chain_kernel, or chain_wide_kernel from 128 "
+                   "(sequence, head) pairs; chunk_table_kernel for packed input)")
 HEADLINE = "varlen_64"
 
 

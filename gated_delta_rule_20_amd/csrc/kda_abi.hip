@@ -218,6 +218,7 @@ kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *a, void *stream)
     char *ws = (char *)a->workspace;
     p.chunk_off = pl.varlen ? (int32_t *)ws : nullptr;
     p.order = pl.varlen ? (int32_t *)ws + (pl.N + 1) : nullptr;
+    p.span = pl.varlen ? (int32_t *)ws + (2 * pl.N + 1) : nullptr;
     p.blocks = ws ? ws + pl.table : nullptr;
     p.n_chunks_cap = has_tokens ? pl.n_chunks_cap : 0;
     p.ckpt = a->checkpoints;

@@ -33,6 +33,7 @@ struct PrefillParams {
     void *o;                            // [rows, H, Dv]
     int32_t *chunk_off;                 // [N+1] (varlen; workspace)
     int32_t *order;                     // [N]   (varlen; workspace)
+    int32_t *span;                      // [N][2] clamped (first token, length) (varlen; workspace)
     char *blocks;                       // [H][n_chunks_cap] per-chunk blocks (workspace)
     int n_chunks_cap;
     float *ckpt;                        // [N, ckpt_slots, H, Dk, Dv] or null
@@ -56,11 +57,11 @@ size_t block_bytes(int bf16, int Dk, int Dv);
 // Bytes of the chunk table at the front of the workspace (0 when !varlen).
 inline size_t table_bytes(int varlen, int N)
 {
-    return varlen ? ((size_t)(2 * N + 1) * sizeof(int32_t) + 255) / 256 * 256 : 0;
+    return varlen ? ((size_t)(4 * N + 1) * sizeof(int32_t) + 255) / 256 * 256 : 0;
 }
 
 // Enqueue the full prefill on `stream`.  The caller has validated arguments
-// and carved the workspace into p.chunk_off / p.order / p.blocks.
+// and carved the workspace into p.chunk_off / p.order / p.span / p.blocks.
 hipError_t launch_chunk_fwd(int bf16, int Dk, int Dv, const PrefillParams &p, hipStream_t stream);
 
 // Speculative-decoding step with replay (one pass over the in-place state).

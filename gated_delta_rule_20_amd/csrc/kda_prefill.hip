@@ -42,6 +42,7 @@
 // belongs to a product exp(lam_r - lam_i) below the smallest normal float.
 #include "kda_common.h"
 #include "kda_prefill.h"
+#include "kda_table.h"
 
 namespace kda {
 
@@ -91,46 +92,29 @@ size_t block_bytes(int bf16_, int Dk, int Dv)
 }
 
 // -----------------------------------------------------------------------------
-// Packed sequences: chunk_off[s] = sum_{s' < s} ceil(len_s' / 64); order =
-// sequences by decreasing length (ties by index) when N <= 2048, else
-// identity.  One workgroup of 1024 threads.
+// Packed sequences: the chunk table (layout and clamping in kda_table.h).  One
+// workgroup of table::THREADS threads; the chunk counts are scanned in LDS in
+// 64-bit, so no sum overflows before it saturates at the capacity.
 // -----------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t *__restrict__ cu, int N,
-                                                           int32_t *__restrict__ chunk_off,
-                                                           int32_t *__restrict__ order)
+__global__ __launch_bounds__(table::THREADS) void chunk_table_kernel(const int32_t *__restrict__ cu, int N, int T,
+                                                                    int cap, int32_t *__restrict__ chunk_off,
+                                                                    int32_t *__restrict__ order,
+                                                                    int32_t *__restrict__ span)
 {
-    __shared__ int part[1024];
+    __shared__ long long part[table::THREADS];
     const int t = threadIdx.x;
-    const int per = (N + 1023) / 1024;
-    const int s0 = min(N, t * per), s1 = min(N, s0 + per);
-    int local = 0;
-    for (int s = s0; s < s1; ++s) local += (cu[s + 1] - cu[s] + CHUNK - 1) / CHUNK;
+    const long long local = table::count(cu, N, T, t, span);
     part[t] = local;
     __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan
-        const int add = (t >= d) ? part[t - d] : 0;
+    for (int d = 1; d < table::THREADS; d <<= 1) {  // inclusive scan
+        const long long add = (t >= d) ? part[t - d] : 0;
         __syncthreads();
         part[t] += add;
         __syncthreads();
     }
-    int run = part[t] - local;
-    for (int s = s0; s < s1; ++s) {
-        chunk_off[s] = run;
-        run += (cu[s + 1] - cu[s] + CHUNK - 1) / CHUNK;
-    }
-    if (t == 1023) chunk_off[N] = part[1023];
-    for (int s = t; s < N; s += 1024) {
-        int rank = s;
-        if (N <= 2048) {
-            const int ls = cu[s + 1] - cu[s];
-            rank = 0;
-            for (int y = 0; y < N; ++y) {
-                const int ly = cu[y + 1] - cu[y];
-                rank += (ly > ls) || (ly == ls && y < s);
-            }
-        }
-        order[rank] = s;
-    }
+    table::offsets(cu, N, T, cap, t, part[t] - local, chunk_off);
+    if (t == table::THREADS - 1) chunk_off[N] = part[t] < cap ? (int)part[t] : cap;
+    for (int s = t; s < N; s += table::THREADS) order[table::rank(cu, N, T, s)] = s;
 }
 
 // -----------------------------------------------------------------------------
@@ -303,8 +287,9 @@ __device__ __forceinline__ bool locate_chunk(const PrefillParams &p, int c, int 
             const int mid = (lo + hi + 1) >> 1;
             if (ld_uniform(p.chunk_off, mid) <= c) lo = mid; else hi = mid - 1;
         }
-        tok0 = ld_uniform(p.cu, lo) + (c - ld_uniform(p.chunk_off, lo)) * CHUNK;
-        len = min(CHUNK, ld_uniform(p.cu, lo + 1) - tok0);
+        const int start = ld_uniform(p.span, 2 * lo);
+        tok0 = start + (c - ld_uniform(p.chunk_off, lo)) * CHUNK;
+        len = min(CHUNK, start + ld_uniform(p.span, 2 * lo + 1) - tok0);
     } else {
         const int cps = (p.T + CHUNK - 1) / CHUNK;
         const int s = c / cps, lc = c - s * cps;
@@ -326,17 +311,16 @@ __device__ __forceinline__ bool locate_seq(const PrefillParams &p, int c, int &t
             const int mid = (lo + hi + 1) >> 1;
             if (ld_uniform(p.chunk_off, mid) <= c) lo = mid; else hi = mid - 1;
         }
-        const int start = ld_uniform(p.cu, lo);
         sq = lo;
         lc = c - ld_uniform(p.chunk_off, lo);
-        slen = ld_uniform(p.cu, lo + 1) - start;
+        slen = ld_uniform(p.span, 2 * lo + 1);
     } else {
         const int cps = (p.T + CHUNK - 1) / CHUNK;
         sq = c / cps;
         lc = c - sq * cps;
         slen = p.T;
     }
-    tok0 = (p.varlen ? ld_uniform(p.cu, sq) : sq * p.T) + lc * CHUNK;
+    tok0 = (p.varlen ? ld_uniform(p.span, 2 * sq) : sq * p.T) + lc * CHUNK;
     len = min(CHUNK, slen - lc * CHUNK);
     return true;
 }
@@ -821,8 +805,8 @@ __global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
     int s, tok0, len, chunk0, nch;
     if (p.varlen) {
         s = p.order[srank];
-        tok0 = p.cu[s];
-        len = p.cu[s + 1] - tok0;
+        tok0 = p.span[2 * s];
+        len = p.span[2 * s + 1];
         chunk0 = p.chunk_off[s];
         nch = p.chunk_off[s + 1] - chunk0;
     } else {
@@ -997,8 +981,8 @@ __global__ __launch_bounds__(256) void chain_wide_kernel(PrefillParams p)
     int s, tok0, len, chunk0, nch;
     if (p.varlen) {
         s = p.order[srank];
-        tok0 = p.cu[s];
-        len = p.cu[s + 1] - tok0;
+        tok0 = p.span[2 * s];
+        len = p.span[2 * s + 1];
         chunk0 = p.chunk_off[s];
         nch = p.chunk_off[s + 1] - chunk0;
     } else {
@@ -1419,7 +1403,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void empty_conv_state_kernel(const PrefillParams p, int C)
 {
     const int s = blockIdx.x / p.H, h = blockIdx.x % p.H;
-    const int slen = p.varlen ? p.cu[s + 1] - p.cu[s] : p.T;
+    const int slen = p.varlen ? p.span[2 * s + 1] : p.T;
     if (slen != 0) return;
     const size_t n = (size_t)(p.f.conv_w - 1) * C, base = ((size_t)s * p.H + h) * n;
     for (size_t e = threadIdx.x; e < n; e += blockDim.x)
@@ -1451,7 +1435,8 @@ template <typename T, int DK, int DV>
 static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
 {
     if (p.varlen)
-        hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, p.cu, p.N, p.chunk_off, p.order);
+        hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(table::THREADS), 0, st, p.cu, p.N, p.T, p.n_chunks_cap,
+                           p.chunk_off, p.order, p.span);
     const bool pro = p.f.conv_w > 0;
     if (pro && p.n_chunks_cap > 0)
         hipLaunchKernelGGL((prologue_kernel<T, DK, DV>), dim3((unsigned)p.n_chunks_cap, (unsigned)p.H), dim3(256), 0, st, p);

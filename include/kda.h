@@ -34,7 +34,10 @@
  *     eq. (5) gate is applied inside the kernels in fp32.
  *   - Preconditions not checked on the device: q and k rows have L2 norm <= 1
  *     (eq. (2) normalises them), beta in [0, 1], cu_seqlens non-decreasing
- *     from 0 to T.
+ *     from 0 to T.  Offsets that break the last one give wrong results but no
+ *     access outside the caller's tensors or the workspace: each sequence is
+ *     clamped into tokens [0, T] (a decreasing pair is an empty sequence) and
+ *     the chunk count saturates at the workspace's capacity.
  *   - The library is thread-safe; calls that share output buffers race.
  */
 #ifndef KDA_H_
