@@ -16,11 +16,11 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_step", "recurrent_replay", "chunk_fwd_workspace_size", "load_library",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "NOALLOC_WORKSPACE_BYTES", "recurrent_step", "recurrent_replay", "chunk_fwd_workspace_size", "load_library",
            "Fusion", "KDAError", "LIB_PATH", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
-EXPORTED_SYMBOLS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_recurrent_step",
+EXPORTED_SYMBOLS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_recurrent_step",
                     "kda_recurrent_replay", "kda_status_string", "kda_last_error_message")
 
 KDA_F32, KDA_BF16 = 0, 1
@@ -157,6 +157,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkFwdArgs), ctypes.c_void_p]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkFwdArgs), ctypes.c_void_p]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_void_p]
     lib.kda_recurrent_step.restype = ctypes.c_int
     lib.kda_recurrent_replay.argtypes = [ctypes.POINTER(ReplayArgs), ctypes.c_void_p]
@@ -254,7 +256,7 @@ def chunk_fwd(q, k, v, g, beta, *, A_log=None, g_min: float = -5.0, scale: float
               cu_seqlens=None, initial_state=None, output_final_state: bool = True,
               out=None, final_state=None, workspace=None, stream=None,
               checkpoints=None, checkpoint_every: int = 0, fusion: Fusion | None = None):
-    """Chunkwise-parallel KDA forward.
+    """Chunkwise-parallel KDA forward (``kda_chunk_fwd``).
 
     q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H] (bf16 or fp32).
     With cu_seqlens ([N+1] int32 on device) the token axis is packed: pass
@@ -303,19 +305,42 @@ def chunk_fwd(q, k, v, g, beta, *, A_log=None, g_min: float = -5.0, scale: float
             raise ValueError(f"checkpoints must be [N, slots >= 1, H, Dk, Dv] with N, H, Dk, Dv = "
                              f"{(N, H, Dk, Dv)} and checkpoint_every >= 1; got {tuple(checkpoints.shape)}, "
                              f"every={checkpoint_every}")
-    need = chunk_fwd_workspace_size(q, v, cu_seqlens=cu_seqlens, N=N,
-                                    prologue=fusion is not None and fusion.prologue)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is _NO_WORKSPACE:  # kda_chunk_fwd_noalloc: the library's own fixed array
+        fn, workspace, ws_bytes = "kda_chunk_fwd_noalloc", None, 0
+    else:
+        fn = "kda_chunk_fwd"
+        need = chunk_fwd_workspace_size(q, v, cu_seqlens=cu_seqlens, N=N,
+                                        prologue=fusion is not None and fusion.prologue)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a = _chunk_args(q, k, v, g, beta, A_log, g_min, scale, cu_seqlens, N, initial_state,
                     out, final_state, workspace, ws_bytes, checkpoints, checkpoint_every)
     if fusion is not None:
         fa = fusion._args(N, H, Dk, Dv, q.dtype, out.shape,
                           slots=None if checkpoints is None else checkpoints.shape[1])
         a.fusion = ctypes.pointer(fa)
-    _check(lib, "kda_chunk_fwd", lib.kda_chunk_fwd(ctypes.byref(a), _stream(stream, q.device)))
+    _check(lib, fn, getattr(lib, fn)(ctypes.byref(a), _stream(stream, q.device)))
     return out, final_state
+
+
+_NO_WORKSPACE = object()
+NOALLOC_WORKSPACE_BYTES = 64 << 20  # KDA_NOALLOC_WORKSPACE_BYTES
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, *, out, final_state=None, A_log=None, g_min: float = -5.0,
+                      scale: float = 1.0, cu_seqlens=None, initial_state=None, stream=None,
+                      checkpoints=None, checkpoint_every: int = 0, fusion: Fusion | None = None):
+    """``kda_chunk_fwd_noalloc``: :func:`chunk_fwd` with the library's fixed
+    device workspace (NOALLOC_WORKSPACE_BYTES per device) instead of one the
+    caller provides.  Nothing is allocated: ``out`` is required and
+    ``final_state`` is written only when given.  Shapes that need a larger
+    workspace raise KDAError (KDA_ERROR_WORKSPACE).  Calls that overlap on one
+    device share the array and race."""
+    return chunk_fwd(q, k, v, g, beta, A_log=A_log, g_min=g_min, scale=scale, cu_seqlens=cu_seqlens,
+                     initial_state=initial_state, output_final_state=False, out=out,
+                     final_state=final_state, workspace=_NO_WORKSPACE, stream=stream,
+                     checkpoints=checkpoints, checkpoint_every=checkpoint_every, fusion=fusion)
 
 
 def recurrent_step(q, k, v, g, beta, state, *, A_log=None, g_min: float = -5.0,

@@ -4,8 +4,16 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "kda.h"
 #include "kda_prefill.h"
+
+// Workspace of kda_chunk_fwd_noalloc: one copy of this array lives on every
+// device that loads the library, for the life of the process.  In host code
+// its name is only a stand-in; the device address comes from
+// hipGetSymbolAddress (once per device, below).
+static __device__ __align__(256) char scratch[KDA_NOALLOC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -141,6 +149,28 @@ kda_status_t hip_fail(hipError_t e, const char *what)
     return fail(KDA_ERROR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Device address of `scratch` on the current device, looked up once per device.
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[MAX_DEVICES];
+
+kda_status_t scratch_on_current_device(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(KDA_ERROR_NOT_SUPPORTED, "device %d beyond %d", dev, MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return KDA_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -240,6 +270,28 @@ kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *a, void *stream)
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     g_err[0] = 0;
     return KDA_SUCCESS;
+}
+
+kda_status_t kda_chunk_fwd_noalloc(const kda_chunk_fwd_args_t *a, void *stream)
+{
+    if (!a) return fail(KDA_ERROR_INVALID_VALUE, "args is NULL");
+    if (a->workspace || a->workspace_bytes)
+        return fail(KDA_ERROR_INVALID_VALUE, "kda_chunk_fwd_noalloc takes no workspace (set workspace = NULL, "
+                    "workspace_bytes = 0)");
+    ChunkPlan pl;
+    kda_status_t st = plan_chunk(a, &pl);
+    if (st != KDA_SUCCESS) return st;
+    if (pl.total > (size_t)KDA_NOALLOC_WORKSPACE_BYTES)
+        return fail(KDA_ERROR_WORKSPACE, "these shapes need %zu workspace bytes; kda_chunk_fwd_noalloc holds at most "
+                    "%zu (KDA_NOALLOC_WORKSPACE_BYTES): use kda_chunk_fwd with a workspace", pl.total,
+                    (size_t)KDA_NOALLOC_WORKSPACE_BYTES);
+    void *ws = nullptr;
+    st = scratch_on_current_device(&ws);
+    if (st != KDA_SUCCESS) return st;
+    kda_chunk_fwd_args_t b = *a;
+    b.workspace = ws;
+    b.workspace_bytes = (size_t)KDA_NOALLOC_WORKSPACE_BYTES;
+    return kda_chunk_fwd(&b, stream);
 }
 
 kda_status_t kda_recurrent_step(const kda_step_args_t *a, void *stream)

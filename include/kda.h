@@ -20,7 +20,8 @@
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; all tensors are
  *     dense, row-major (last index fastest) and 16-byte aligned.  The library
- *     allocates no device memory and keeps no state between calls.
+ *     allocates no device memory and keeps no state between calls (apart from
+ *     the fixed workspace array of kda_chunk_fwd_noalloc, below).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
  *     No call synchronises the device or copies data to the host.
  *   - Validation happens before anything is enqueued; on error nothing is
@@ -194,6 +195,28 @@ typedef struct {
 KDA_API kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args_t *args, size_t *bytes);
 
 KDA_API kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *args, void *stream);
+
+/*
+ * kda_chunk_fwd without a caller-provided workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It computes exactly what kda_chunk_fwd
+ * computes, with the same kernels, and calls no allocating routine: its
+ * workspace is a fixed array of KDA_NOALLOC_WORKSPACE_BYTES in device memory
+ * that every device the library runs on holds from module load until the
+ * process ends.  args->workspace must be NULL and args->workspace_bytes 0.
+ * Shapes whose kda_chunk_fwd_workspace_size exceeds the array are rejected
+ * with KDA_ERROR_WORKSPACE before anything is enqueued (at bf16 and
+ * Dk = Dv = 128 without the prologue the array holds 897 chunk blocks of
+ * 64 tokens x 1 head, e.g. B = 1, T = 7168 tokens at H = 8).  The array used
+ * is the copy on the device that is current when the call is made, which must
+ * be the stream's device.  Every call on one device uses the same array, so
+ * calls that overlap on a device (on different streams, or from different
+ * threads without ordering) race; calls ordered on one stream do not.  The
+ * array's contents on entry are ignored: every value a call uses from it is
+ * written earlier in the same call, so nothing needs clearing between calls.
+ */
+#define KDA_NOALLOC_WORKSPACE_BYTES (64u << 20)
+KDA_API kda_status_t kda_chunk_fwd_noalloc(const kda_chunk_fwd_args_t *args, void *stream);
 
 /*
  * One decode step for N independent sequences (one token each), eq. (1):

@@ -335,3 +335,35 @@ def test_prologue_workspace_grows(lib):
     rows, H = 128, 2
     al = lambda b: (b + 255) // 256 * 256
     assert out.value == base + 2 * al(rows * H * 128 * 2) + al(rows * H * 128 * 2) + al(rows * H * 2)
+
+
+def test_noalloc_limit_matches_header():
+    m = re.search(r"#define\s+KDA_NOALLOC_WORKSPACE_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == kda.NOALLOC_WORKSPACE_BYTES
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(workspace=0x100000, workspace_bytes=1 << 30), 1, "takes no workspace"),
+    (dict(workspace_bytes=4096), 1, "takes no workspace"),
+    (dict(T=8192, H=32), 3, "holds at most"),
+    (dict(T=7232, H=8), 3, "holds at most"),               # 113 chunks x 8 heads: one chunk over
+    (dict(T=7000, H=8, cu_seqlens=0x20000, N=64), 3, "holds at most"),
+    (dict(Dk=96), 2, "head dims"),
+])
+def test_chunk_fwd_noalloc_rejects_before_device_work(lib, over, status, msg):
+    """Rejections the no-allocation entry point makes on the host, before it
+    touches a device (so they hold on a machine without one)."""
+    a = _args(**over)
+    st = lib.kda_chunk_fwd_noalloc(ctypes.byref(a), None)
+    assert st == status, lib.kda_last_error_message()
+    assert msg in lib.kda_last_error_message().decode()
+    assert lib.kda_chunk_fwd_noalloc(None, None) == 1
+
+
+def test_noalloc_array_holds_the_documented_largest_call(lib):
+    """The header's example: B = 1, T = 7168 at H = 8 (bf16, 128/128) fits,
+    one more chunk does not."""
+    st, n = _ws(lib, _args(T=7168, H=8))
+    assert st == 0 and n <= kda.NOALLOC_WORKSPACE_BYTES
+    st, n = _ws(lib, _args(T=7169, H=8))
+    assert st == 0 and n > kda.NOALLOC_WORKSPACE_BYTES
