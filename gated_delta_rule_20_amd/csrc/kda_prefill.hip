@@ -430,7 +430,9 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 const float t0 = sg[0] + sg[1], t1 = sg[2] + sg[3], t2 = sg[4] + sg[5], t3 = sg[6] + sg[7];
                 const float Bm = (m0 > 0 ? t0 : 0.f) + (m0 > 1 ? t1 : 0.f) + (m0 > 2 ? t2 : 0.f);
                 const float C2 = t0 + t1 + t2 + t3;
-                const float hoff = hf ? sg[2 * m0] : 0.f;          // first half of the tile, for the second half
+                // first half of the tile, for the second half (read from LDS: a
+                // register array indexed by the wave's tile would go to scratch)
+                const float hoff = hf ? sm.tot[2 * m0][ch0 + cc] : 0.f;
 #pragma unroll
                 for (int r = 0; r < HT; ++r) lam2[r][cc] += hoff;
                 eBm[cc] = __builtin_amdgcn_exp2f(Bm);              // exp(B_m)            <= 1
@@ -501,54 +503,6 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         }
         lds_barrier();
 
-        // ---- P2: L and A sub-tiles on MFMA ----------------------------------
-        {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int pi = w + IWAVES * s;  // (m, n) pair m(m+1)/2 + n; waves 0, 1 take two
-                if (pi >= 10) break;
-                const int m = (pi == 0) ? 0 : (pi < 3 ? 1 : (pi < 6 ? 2 : 3));
-                const int n = pi - m * (m + 1) / 2;
-                const int cr = colop_row(m, n);
-                f32x4 aL = {0.f, 0.f, 0.f, 0.f}, aA = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const frag_t<T> kr = load_frag_lin<T>(&sm.ops.KR[16 * m + x][32 * ks], g);
-                    const frag_t<T> qr = load_frag_lin<T>(&sm.ops.QR[16 * m + x][32 * ks], g);
-                    const frag_t<T> kc = load_frag_lin<T>(&sm.y.KC[cr + x][32 * ks], g);
-                    aL = mma(kr, kc, aL);   // rows r (tile m), cols i (tile n)
-                    aA = mma(kc, qr, aA);   // rows i (tile n), cols r (tile m): A^T
-                }
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int row = 16 * m + 4 * g + ii, col = 16 * n + x;
-                    sm.L[row][col] = (col < row) ? sm.beta[row] * aL[ii] : 0.f;
-                }
-                f32x4 a4;
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int r = 16 * m + x, col = 16 * n + 4 * g + ii;
-                    a4[ii] = (col <= r) ? aA[ii] : 0.f;
-                }
-                *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
-                    make_quad<T>(a4);
-            }
-            if (w == 2 || w == 3) {  // the all-zero upper tiles inside used k-steps: (0,1) and (2,3)
-                const int m = (w == 2) ? 0 : 2, n = m + 1;
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
-                    make_quad<T>(z);
-            }
-        }
-        lds_barrier();  // L complete; KR / KC fully read (Tp may overwrite the off-diagonal column operands)
-        // ---- P3: T' = (I + L)^-1 Diag(beta), 16x16 blocks ---------------------
-        // Diagonal blocks D_m = (I + L_mm)^-1 (waves 0-3, below); then wave
-        // n < 3 walks block column n downwards,
-        //   T_mn = -D_m sum_{q=n}^{m-1} L_mq T_qn,   T_nn = D_n,
-        // keeping T_qn in fp32 MFMA accumulators: with k = 4g + i at step i a
-        // lane's accumulator element i is exactly its B operand, so no block
-        // goes back through LDS.  Every block is written once, scaled by beta of
-        // its column and rounded, into the MFMA operand array Tp.
         // Q+ = scale Q Gamma as the chain's operand fragments (rows tokens, k
         // channels in kmap order), from the row operand and exp(B_m); fragment f
         // is token tile f / KS, k-step f % KS.
@@ -565,20 +519,77 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             }
             store8(blk + BL::Q_OFF + ((m * KS + ks) * 64 + l) * 8, qp);
         };
+
+        // ---- P2: L and A sub-tiles on MFMA; diagonal inverses ----------------
+        // Ten (m, n) tile pairs, each an L product (rows r of tile m, columns i
+        // of tile n) and an A^T product.  Waves 0-3 take the diagonal pair
+        // (m, m) = (w, w) and invert their block at once (below); waves 4-7
+        // take the six off-diagonal pairs: one whole each, and (3,1), (3,2)
+        // split by product (waves 4, 5 the L products, waves 6, 7 the A^T
+        // products), then the first half of Q+.  All fragments of a pair are
+        // read from LDS before its first product is issued.
+        //
+        // T' = (I + L)^-1 Diag(beta) by 16x16 blocks: the diagonal blocks
+        // D_m = (I + N)^-1, N = L_mm strictly lower (N^16 = 0), as the finite
+        // product (I - N)(I + N^2)(I + N^4)(I + N^8) on fp32 MFMA (a product X Y
+        // takes Y in accumulator layout and X in row layout, which is X^T in
+        // accumulator layout, so each factor is also kept transposed); then in
+        // P3 wave n < 3 walks block column n downwards,
+        //   T_mn = -D_m sum_{q=n}^{m-1} L_mq T_qn,   T_nn = D_n,
+        // keeping T_qn in fp32 MFMA accumulators: with k = 4g + i at step i a
+        // lane's accumulator element i is exactly its B operand, so no block
+        // goes back through LDS.  Every block is written once, scaled by beta of
+        // its column and rounded, into the MFMA operand array Tp.
+        float(*L)[SM::LP] = sm.L;
+        constexpr int LP = SM::LP;
+        f32x4 dmv = {0.f, 0.f, 0.f, 0.f};  // waves 0-3: D_w in accumulator layout, D[4g+i][x]
         {
-            float(*L)[SM::LP] = sm.L;
-            constexpr int LP = SM::LP;
-            if (w < 4) {
-                // D_m = (I + N)^-1 with N = L_mm strictly lower (N^16 = 0), as the
-                // finite product (I - N)(I + N^2)(I + N^4)(I + N^8) on fp32 MFMA.
-                // A product X Y takes Y in accumulator layout and X in row layout,
-                // which is X^T in accumulator layout; so each factor is also kept
-                // transposed.  Wave m inverts block m.
-                const int o0 = 16 * w;
-                f32x4 nr, na;  // N row layout (lane (x,g): N[x][4g+i]) and accumulator layout (N[4g+i][x])
-                nr = *reinterpret_cast<const f32x4 *>(&L[o0 + x][o0 + 4 * g]);
+            auto pair_products = [&](int m, int n, bool doL, bool doA, f32x4 &aL, f32x4 &aA) {
+                const int cr = colop_row(m, n);
+                frag_t<T> kc[KS], kr[KS], qr[KS];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) na[i] = L[o0 + 4 * g + i][o0 + x];
+                for (int ks = 0; ks < KS; ++ks) kc[ks] = load_frag_lin<T>(&sm.y.KC[cr + x][32 * ks], g);
+                if (doL) {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) kr[ks] = load_frag_lin<T>(&sm.ops.KR[16 * m + x][32 * ks], g);
+                }
+                if (doA) {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) qr[ks] = load_frag_lin<T>(&sm.ops.QR[16 * m + x][32 * ks], g);
+                }
+                aL = f32x4{0.f, 0.f, 0.f, 0.f};
+                aA = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (doL) aL = mma(kr[ks], kc[ks], aL);  // rows r (tile m), cols i (tile n)
+                    if (doA) aA = mma(kc[ks], qr[ks], aA);  // rows i (tile n), cols r (tile m): A^T
+                }
+            };
+            // beta of the row, strictly lower part only (all of an off-diagonal block)
+            auto l_block = [&](int m, int n, const f32x4 &aL) {
+                const f32x4 bt = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * m + 4 * g]);
+                f32x4 v;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) v[ii] = (m != n || x < 4 * g + ii) ? bt[ii] * aL[ii] : 0.f;
+                return v;
+            };
+            auto store_a = [&](int m, int n, const f32x4 &aA) {
+                f32x4 a4;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) a4[ii] = (m != n || 4 * g + ii <= x) ? aA[ii] : 0.f;
+                *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
+                    make_quad<T>(a4);
+            };
+            f32x4 aL, aA;
+            if (w < 4) {
+                const int m = w, o0 = 16 * w;
+                pair_products(m, m, true, true, aL, aA);
+                store_a(m, m, aA);
+                const f32x4 na = l_block(m, m, aL);  // N in accumulator layout (lane (x,g): N[4g+i][x])
+#pragma unroll
+                for (int i = 0; i < 4; ++i) L[o0 + 4 * g + i][o0 + x] = na[i];
+                // N in row layout (lane (x,g): N[x][4g+i]), read back transposed by this wave
+                const f32x4 nr = *reinterpret_cast<const f32x4 *>(&L[o0 + x][o0 + 4 * g]);
                 auto mm = [](const f32x4 &a, const f32x4 &b) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -596,36 +607,61 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 const f32x4 n4 = mm(n2t, n2), n4t = mm(n2, n2t);
                 const f32x4 a3 = a2 + mm(a2t, n4), a3t = a2t + mm(n4, a2t);
                 const f32x4 n8 = mm(n4t, n4);
-                const f32x4 dmv = a3 + mm(a3t, n8);  // D[4g+i][x]
-                const float bc = sm.beta[o0 + x];
+                dmv = a3 + mm(a3t, n8);
                 float *Dm = dblk(sm, w);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    Dm[(4 * g + i) * LP + x] = dmv[i];
-                    sm.y.t.Tp[o0 + 4 * g + i][o0 + x] = from_f<T>(dmv[i] * bc);
-                }
+                for (int i = 0; i < 4; ++i) Dm[(4 * g + i) * LP + x] = dmv[i];
             } else {
-                for (int e = t - 256; e < 6 * 256; e += 64 * (IWAVES - 4)) {  // upper off-diagonal blocks are zero
-                    const int bi = e / 256, a = (e / 16) % 16, b = e % 16;
-                    const int mb = (bi < 3) ? 0 : (bi < 5 ? 1 : 2);
-                    const int nb = (bi < 3) ? bi + 1 : (bi < 5 ? bi - 1 : 3);
-                    sm.y.t.Tp[16 * mb + a][16 * nb + b] = from_f<T>(0.f);
+                const int j = w - 4;
+                {  // (1,0), (2,0), (2,1), (3,0)
+                    const int m = j == 0 ? 1 : (j == 3 ? 3 : 2), n = j == 2 ? 1 : 0;
+                    pair_products(m, n, true, true, aL, aA);
+                    const f32x4 v = l_block(m, n, aL);
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) L[16 * m + 4 * g + ii][16 * n + x] = v[ii];
+                    store_a(m, n, aA);
                 }
-                for (int f = w - 4; f < 2 * KS; f += IWAVES - 4) qp_frag(f);  // first half of Q+
+                {
+                    const int m = 3, n = 1 + (j & 1);
+                    const bool doL = j < 2;
+                    pair_products(m, n, doL, !doL, aL, aA);
+                    if (doL) {
+                        const f32x4 v = l_block(m, n, aL);
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii) L[16 * m + 4 * g + ii][16 * n + x] = v[ii];
+                    } else {
+                        store_a(m, n, aA);
+                    }
+                }
+                if (j < 2) {  // the all-zero upper A tiles inside used k-steps: (0,1) and (2,3)
+                    const int m = 2 * j, n = m + 1;
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
+                        make_quad<T>(z);
+                }
+                for (int f = j; f < 2 * KS; f += IWAVES - 4) qp_frag(f);  // first half of Q+
             }
-            lds_barrier();
+        }
+        lds_barrier();  // L and D complete; KR / KC fully read (Tp may overwrite the off-diagonal column operands)
+
+        // ---- P3: off-diagonal blocks of T'; K~^T and the rest of Q+ ----------
+        {
             // The next item's raw inputs were loaded during P1, two phases ago; wait
             // for them here, where the only younger memory operations are this
             // item's early result stores.  Loads and stores share one counter, so
             // a wait at the top of the next item would also wait for every P3/P4
             // store.
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
+            if (w < 4) {  // diagonal block of Tp
+                const float bc = sm.beta[16 * w + x];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.y.t.Tp[16 * w + 4 * g + i][16 * w + x] = from_f<T>(dmv[i] * bc);
+            }
             if (w < 3) {
                 const int n = w;
                 const float bc = sm.beta[16 * n + x];
                 f32x4 Tr[4];  // Tr[d] = T_{n+d, n}: rows 4g + i, column x
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Tr[0][i] = dblk(sm, n)[(4 * g + i) * LP + x];
+                Tr[0] = dmv;
 #pragma unroll
                 for (int d = 1; d < 4; ++d) {
                     if (n + d > 3) break;
@@ -646,6 +682,15 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     for (int i = 0; i < 4; ++i) sm.y.t.Tp[16 * m + 4 * g + i][16 * n + x] = from_f<T>(Tr[d][i] * bc);
                 }
             } else {
+                // Of the zero upper blocks of Tp, P4 reads only (0,1) and (2,3)
+                // (inside its 32-wide k-steps of row tiles 0 and 2).
+                if (w == 4 || w == 5) {
+                    const int mb = (w == 4) ? 0 : 2, r = l >> 2, cq = 4 * (l & 3);
+                    tok4 z;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) z[e] = from_f<T>(0.f);
+                    *reinterpret_cast<tok4 *>(&sm.y.t.Tp[16 * mb + r][16 * (mb + 1) + cq]) = z;
+                }
                 // (K gamma^C / Gamma)^T as the chain's A-operand fragments (rows
                 // channels, k tokens in kmap order), copied from LDS.
                 for (int f = w - 3; f < 2 * (DK / 16); f += IWAVES - 3) {
@@ -658,25 +703,38 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         lds_barrier();
 
         // ---- P4: U = T' V and W^T = K+^T T'^T on MFMA -------------------------
-        for (int ct = w; ct < DV / 16; ct += IWAVES) {
+        // The Tp fragments (row tile m, k-step ks <= m / 2) are the A operands of
+        // U and the B operands of W^T: read once per wave.
+        if (w < (DV > DK ? DV : DK) / 16) {
+            frag_t<T> tpf[4][2];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int ks = 0; ks <= m / 2; ++ks)
-                    acc = mma(load_frag_lin<T>(&sm.y.t.Tp[16 * m + x][32 * ks], g),
-                              load_frag_lin<T>(&sm.VT[16 * ct + x][32 * ks], g), acc);
-                *reinterpret_cast<quad_t<T> *>(blk + BL::U_OFF + ((ct * 4 + m) * 64 + l) * 4) = make_quad<T>(acc);
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int ks = 0; ks <= m / 2; ++ks) tpf[m][ks] = load_frag_lin<T>(&sm.y.t.Tp[16 * m + x][32 * ks], g);
+            for (int ct = w; ct < DV / 16; ct += IWAVES) {
+                frag_t<T> vt[2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) vt[ks] = load_frag_lin<T>(&sm.VT[16 * ct + x][32 * ks], g);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks <= m / 2; ++ks) acc = mma(tpf[m][ks], vt[ks], acc);
+                    *reinterpret_cast<quad_t<T> *>(blk + BL::U_OFF + ((ct * 4 + m) * 64 + l) * 4) = make_quad<T>(acc);
+                }
             }
-        }
-        for (int ct = w; ct < DK / 16; ct += IWAVES) {
+            for (int ct = w; ct < DK / 16; ct += IWAVES) {
+                frag_t<T> kp[2];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int ks = 0; ks <= tt / 2; ++ks)
-                    acc = mma(load_frag_lin<T>(&sm.KpT[16 * ct + x][32 * ks], g),
-                              load_frag_lin<T>(&sm.y.t.Tp[16 * tt + x][32 * ks], g), acc);
-                *reinterpret_cast<quad_t<T> *>(blk + BL::W_OFF + ((tt * KS + ct / 2) * 64 + l) * 8 + 4 * (ct % 2)) =
-                    make_quad<T>(-acc);
+                for (int ks = 0; ks < 2; ++ks) kp[ks] = load_frag_lin<T>(&sm.KpT[16 * ct + x][32 * ks], g);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks <= tt / 2; ++ks) acc = mma(kp[ks], tpf[tt][ks], acc);
+                    *reinterpret_cast<quad_t<T> *>(blk + BL::W_OFF + ((tt * KS + ct / 2) * 64 + l) * 8 + 4 * (ct % 2)) =
+                        make_quad<T>(-acc);
+                }
             }
         }
         lds_barrier();  // LDS is reused by the next item
