@@ -147,10 +147,11 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
-// eq. (5) gate in fp32: g = g_min * sigmoid(exp(A_h) * z), with eA = exp(A_h).
+// eq. (5) gate in fp32: g = g_min * sigmoid(exp(A_h) * z), with eA = exp(A_h);
+// the sigmoid's reciprocal on the hardware reciprocal (about 1 ulp).
 __device__ __forceinline__ float gate_from_logit(float z, float eA, float g_min) {
     const float x = eA * z;
-    return g_min / (1.0f + __expf(-x));
+    return g_min * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
 // 1 / sqrt(x) for the L2Norm / RMSNorm denominators (x = sum or mean of squares

@@ -86,6 +86,29 @@ template <int V, int W = 1> __device__ __forceinline__ void upd16(float *x, floa
         : "v"(kr), "v"(d), "i"(W));
 }
 
+// Cross-lane sums without LDS.  wave_sum: the sum over the 64 lanes of a wave,
+// returned uniform, from DPP steps (pairs, quads, 8- and 16-lane rows, then
+// row broadcasts into rows 1-3; lane 63 ends with the total).  pair_sum32:
+// v[l] + v[l ^ 32] in every lane.
+template <int CTRL, int ROWS> __device__ __forceinline__ float dpp_add(float v)
+{
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);  // row_mirror: every lane holds its 16-lane row's sum
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float pair_sum32(float v)
+{
+    return v + __shfl_xor(v, 32);
+}
+
 // One workgroup per (sequence, head).  Each state column is held by NH = d_k/64
 // lanes of one wave (lanes l and l + 32 when NH = 2), each with 64 rows of it
 // in registers.  A token's two reductions over the rows, p = (D S)^T k and
@@ -125,7 +148,8 @@ template <int V, int W = 1> __device__ __forceinline__ void upd16(float *x, floa
 // the block, each wave sums o~^2 over the head's d_v columns for each token and
 // the thread of column c writes Sigmoid(gate) * w_c * o~_c / rms.
 template <typename T, int DK, int DV, int TB, bool FU>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(((TB > 1 && !FU) || (TB == 1 && FU)) ? 4 : 3))) void replay_kernel(ReplayParams p)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    (TB == 1 && !FU) ? 3 : ((!FU || TB == 1 || DV * (DK / 64) >= DK + DV) ? 4 : 3)))) void replay_kernel(ReplayParams p)
 {
     constexpr int NH = DK / 64;         // lanes per column
     constexpr int RH = 64;              // rows per lane
@@ -134,6 +158,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(((TB > 1 &&
     constexpr int NW = NT / 64;         // waves
     constexpr int CC = 2 * DK + DV;     // convolution channels per head
     constexpr bool RB = TB > 1 || FU;  // row-broadcast token loop (all but the plain single step)
+    // Fused staging split by role when the workgroup has a thread per channel of
+    // each kind: waves 0 .. DK/64 - 1 take the query / key / decay channels, the
+    // other waves the value / output-gate channels.
+    constexpr bool SPLIT = FU && NT >= DK + DV;
     static_assert(NH * RH == DK && NT % 64 == 0 && NT <= 256 && NT >= DK && NT >= DV, "shape");
     __shared__ __align__(16) float s_kd[TB][DK], s_qd[TB][DK], s_ki[TB][DK];  // P_j k, P_j q, k / P_j
     __shared__ __align__(16) float s_pc[DK], s_pe[DK];    // P at the commit token, P at the block end
@@ -141,7 +169,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(((TB > 1 &&
     constexpr int FT = FU ? TB : 1, FV = FU ? DV : 1, FW = FU ? NW : 1;
     __shared__ float s_sk[FW][FT], s_sq[FW][FT];          // partial sums of a_k^2, a_q^2 (prologue)
     __shared__ float s_o[FT][FV], s_gt[FT][FV];           // o~ and Sigmoid(gate) of the block (epilogue)
-    __shared__ float s_hist[FU ? 3 : 1][FU ? CC : 1];     // conv history between blocks (prologue)
+    constexpr bool GH = FU && !(NT >= DK + DV);           // generic fused staging
+    __shared__ float s_hist[GH ? 3 : 1][GH ? CC : 1];     // conv history between blocks (prologue, generic staging)
 
     // (the fused variant keeps the wave index in a scalar: its per-wave LDS slots
     // then need no per-lane address registers)
@@ -181,7 +210,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(((TB > 1 &&
     const bool pro = FU && p.f.conv_w > 0, epi = FU && p.f.gate != nullptr;
     const int cw = pro ? p.f.conv_w : 1;
     T *const cstate = (FU && cw > 1) ? (T *)p.f.conv_state + nh * (size_t)((cw - 1) * CC) : nullptr;
-    if constexpr (FU) {
+    // Split staging: the history of this thread's channels stays in registers
+    // (h0: query or value channel, h1: key channel), the carried state's rows
+    // loaded here and converted in the first block's staging, so that waiting
+    // for them does not hold back the first block's input loads.
+    T hr0[3], hr1[3];
+    float h0[3] = {0.f, 0.f, 0.f}, h1[3] = {0.f, 0.f, 0.f};
+    if constexpr (SPLIT) {
+        const bool kr = t < DK;
+        const unsigned c0 = kr ? (unsigned)t : DK + (unsigned)t, c1 = DK + (unsigned)t;  // q and k, or v = 2 DK + (t - DK)
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int j = i - 4 + cw;
+            const bool in = pro && cstate && j >= 0;
+            const T *cr = in ? cstate + j * CC : nullptr;
+            hr0[i] = in ? cr[c0] : from_f<T>(0.f);
+            hr1[i] = (in && kr) ? cr[c1] : from_f<T>(0.f);
+        }
+    } else if constexpr (FU) {
         if (pro) {
 #pragma unroll
             for (int i = 0; i < 3; ++i) {     // slot i holds state row i - 4 + cw (if any)
@@ -201,7 +247,126 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(((TB > 1 &&
         const int jc = commit_at - 1 - base;      // commit token inside this block, if 0 <= jc < nb
         // ---- stage the block's inputs: all loads first (one latency per block),
         // then the per-row products into LDS ----
-        {
+        if constexpr (SPLIT) {
+            int tl = t;
+            asm volatile("" : "+v"(tl));  // addresses formed here, not kept from before the block loop
+            const bool kr = tl < DK;      // wave-uniform role
+            const int ch = kr ? tl : tl - DK;
+            // Per-lane offsets are unsigned 32-bit so that every global access is a
+            // uniform base plus a zero-extended lane offset (no 64-bit lane addresses).
+            const unsigned uch = (unsigned)ch;
+            const unsigned c0 = kr ? uch : 2u * DK + uch, c1 = DK + uch;  // conv channels: q and k, or v
+            float w0[4] = {0.f, 0.f, 0.f, 0.f}, w1[4] = {0.f, 0.f, 0.f, 0.f};
+            if (pro) {
+                if (base == 0) {
+#pragma unroll
+                    for (int i = 0; i < 3; ++i) {
+                        h0[i] = to_f<T>(hr0[i]);
+                        h1[i] = to_f<T>(hr1[i]);
+                    }
+                }
+                const float *wb = p.f.conv_weight + (size_t)h * CC * cw;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {  // tap i holds weight i - 4 + cw (if any)
+                    const int x = i - 4 + cw;
+                    if (x >= 0) {
+                        const float *wx = wb + x;
+                        w0[i] = wx[c0 * (unsigned)cw];
+                        if (kr) w1[i] = wx[c1 * (unsigned)cw];
+                    }
+                }
+            }
+            float pr = 1.f;                      // running product of alpha (query / key role)
+            // SB tokens at a time: their loads together, then their products.  Sigmoids
+            // and 1 / P use the hardware reciprocal (about 1 ulp).
+            constexpr int SB = TB < 4 ? TB : 4;
+            for (int j0 = 0; j0 < nb; j0 += SB) {
+                // query / key role: decay logit, key, query; value role: value, output gate
+                T a0[SB], a1[SB], a2[SB];
+                float bt[SB];
+#pragma unroll
+                for (int jj = 0; jj < SB; ++jj) {
+                    const int j = j0 + jj, it = base + j;
+                    const bool ok = j < nb, rep = it < n_rep;
+                    const size_t row = ok ? row_of(it) : 0;
+                    if (kr) {
+                        const T *gb = (const T *)(rep ? p.g_r : p.g) + row * DK;
+                        const T *kb = (const T *)(rep ? p.k_r : p.k) + row * DK;
+                        const T *qb = (const T *)(rep ? p.q_r : p.q) + row * DK;
+                        a0[jj] = ok ? gb[uch] : from_f<T>(0.f);
+                        a1[jj] = ok ? kb[uch] : from_f<T>(0.f);
+                        // with the prologue the replayed queries feed the convolution
+                        a2[jj] = (ok && (pro || !rep)) ? qb[uch] : from_f<T>(0.f);
+                    } else {
+                        const T *vb = (const T *)(rep ? p.v_r : p.v) + row * DV;
+                        const T *eb = (const T *)p.f.gate + row * DV;
+                        a0[jj] = ok ? vb[uch] : from_f<T>(0.f);
+                        a1[jj] = (epi && ok && !rep) ? eb[uch] : from_f<T>(0.f);
+                        a2[jj] = from_f<T>(0.f);
+                    }
+                    bt[jj] = ok ? to_f<T>(((const T *)(rep ? p.beta_r : p.beta))[row]) : 0.f;
+                }
+#pragma unroll
+                for (int jj = 0; jj < SB; ++jj) {
+                    const int j = j0 + jj;
+                    if (j >= nb) break;
+                    float kq = 0.f, ssk = 0.f, ssq = 0.f;
+                    // ShortConv + Swish (eq. (2)) of channel c0 (and c1); the history advances
+                    const float x0 = to_f<T>(kr ? a2[jj] : a0[jj]), x1 = to_f<T>(a1[jj]);
+                    float y0 = x0, y1 = x1;
+                    if (pro) {
+                        float c0v = w0[3] * x0, c1v = w1[3] * x1;
+#pragma unroll
+                        for (int i = 0; i < 3; ++i) {
+                            c0v += w0[i] * h0[i];
+                            c1v += w1[i] * h1[i];
+                        }
+                        h0[0] = h0[1]; h0[1] = h0[2]; h0[2] = x0;
+                        h1[0] = h1[1]; h1[1] = h1[2]; h1[2] = x1;
+                        y0 = c0v * __builtin_amdgcn_rcpf(1.f + __expf(-c0v));
+                        y1 = c1v * __builtin_amdgcn_rcpf(1.f + __expf(-c1v));
+                        if (j == jc && cstate) {  // committed: carry the last cw - 1 pre-activations
+#pragma unroll
+                            for (int i = 0; i < 3; ++i) {
+                                const int r = i - 4 + cw;
+                                if (r >= 0) {
+                                    T *cr = cstate + r * CC;
+                                    cr[c0] = from_f<T>(h0[i]);
+                                    if (kr) cr[c1] = from_f<T>(h1[i]);
+                                }
+                            }
+                        }
+                    }
+                    if (kr) {  // y0 = a_q, y1 = a_k
+                        float g = to_f<T>(a0[jj]);
+                        g = p.A_log ? gate_from_logit(g, eA, p.g_min) : clamp_logdecay(g, p.g_min);
+                        pr *= __expf(g);
+                        s_kd[j][ch] = pr * y1;
+                        s_qd[j][ch] = pr * y0;
+                        s_ki[j][ch] = y1 * __builtin_amdgcn_rcpf(pr);
+                        if (j == jc) s_pc[ch] = pr;
+                        if (j == nb - 1) s_pe[ch] = pr;
+                        kq = y1 * y0;
+                        ssk = y1 * y1;
+                        ssq = y0 * y0;
+                    } else {   // y0 = value after the prologue
+                        s_v[j][ch] = y0;
+                        if (epi) s_gt[j][ch] = __builtin_amdgcn_rcpf(1.f + __expf(-x1));
+                    }
+                    kq = wave_sum(kq);
+                    if (l == 0) s_kqw[w][j] = kq;
+                    if (pro) {
+                        ssk = wave_sum(ssk);
+                        ssq = wave_sum(ssq);
+                        if (l == 0) {
+                            s_sk[FU ? w : 0][FU ? j : 0] = ssk;
+                            s_sq[FU ? w : 0][FU ? j : 0] = ssq;
+                        }
+                    }
+                    if (tl == 0) s_b[j] = pro ? __builtin_amdgcn_rcpf(1.f + __expf(-bt[jj])) : bt[jj];
+                }
+            }
+        } else {
             constexpr int RPT = (DK + NT - 1) / NT;  // staged rows per thread
             constexpr int CPT = (DV + NT - 1) / NT;  // staged value columns per thread
             static_assert(!FU || (RPT == 1 && CPT == 1), "prologue staging assumes one row and one column per thread");
@@ -332,16 +497,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(((TB > 1 &&
                         }
                     }
                 }
-#pragma unroll
-                for (int m = 32; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
+                kq = wave_sum(kq);
                 if (l == 0) s_kqw[w][j] = kq;
                 if constexpr (FU) {
                     if (pro) {
-#pragma unroll
-                        for (int m = 32; m >= 1; m >>= 1) {
-                            ssk += __shfl_xor(ssk, m);
-                            ssq += __shfl_xor(ssq, m);
-                        }
+                        ssk = wave_sum(ssk);
+                        ssq = wave_sum(ssq);
                         if (l == 0) {
                             s_sk[w][j] = ssk;
                             s_sq[w][j] = ssq;
@@ -427,8 +588,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(((TB > 1 &&
                 }
             }
             if (NH == 2) {                        // the other 64 rows of the column
-                pp += __shfl_xor(pp, 32);
-                if (!rep) rr += __shfl_xor(rr, 32);
+                pp = pair_sum32(pp);
+                if (!rep) rr = pair_sum32(rr);
             }
             if constexpr (FU) {
                 pp *= nk;
@@ -490,8 +651,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(((TB > 1 &&
                     float ss = 0.f;
 #pragma unroll
                     for (int c = 0; c < DV; c += 64) ss += s_o[j][c + le] * s_o[j][c + le];
-#pragma unroll
-                    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+                    ss = wave_sum(ss);
                     if (te < DV) {
                         const float y = s_gt[j][te] * wo * s_o[j][te] * rsq_norm(ss * (1.f / DV) + p.f.o_eps);
                         ((T *)p.o)[row_of(base + j) * DV + te] = from_f<T>(y);
