@@ -236,7 +236,7 @@ def _chunk_args(q, k, v, g, beta, A_log, g_min, scale, cu_seqlens, N, h0, o, hT,
 def chunk_fwd_workspace_size(q, v, *, cu_seqlens=None, N=None, prologue: bool = False) -> int:
     """Workspace bytes kda_chunk_fwd needs for q [B,T,H,Dk] (or [T,H,Dk] with
     cu_seqlens) and v [..., Dv]; ``prologue``: a fusion with the eq. (2)
-    prologue on (it adds room for the convolved q, k, v, beta)."""
+    prologue on (passed through; the prologue needs no workspace)."""
     lib = load_library()
     n = (cu_seqlens.numel() - 1) if cu_seqlens is not None else 0
     a = _chunk_args(q, q, v, q, q, None, -5.0, 1.0, cu_seqlens, N if N is not None else n,

@@ -104,7 +104,7 @@ kda_status_t check_fusion(const kda_layer_fusion_t *f, bool prefill, bool has_ck
 struct ChunkPlan {
     int varlen, N, rows;
     int n_chunks_cap;
-    size_t table, block, blocks, pro, total;
+    size_t table, block, blocks, total;
 };
 
 kda_status_t plan_chunk(const kda_chunk_fwd_args_t *a, ChunkPlan *pl)
@@ -138,9 +138,7 @@ kda_status_t plan_chunk(const kda_chunk_fwd_args_t *a, ChunkPlan *pl)
     pl->table = kda::table_bytes(pl->varlen, pl->N);
     pl->block = block;
     pl->blocks = (size_t)a->H * (size_t)cap * block;
-    const int pro = a->fusion && a->fusion->conv_width > 0;
-    pl->pro = kda::prologue_bytes(pro, rows, a->H, a->Dk, a->Dv, a->dtype == KDA_BF16 ? 2 : 4);
-    pl->total = pl->table + pl->blocks + pl->pro;
+    pl->total = pl->table + pl->blocks;  // the layer prologue needs no workspace (it runs in registers)
     return KDA_SUCCESS;
 }
 
@@ -255,17 +253,6 @@ kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *a, void *stream)
     p.ckpt_every = a->checkpoints ? a->checkpoint_every : 0;
     p.ckpt_slots = a->checkpoints ? a->checkpoint_slots : 0;
     p.f = fp;
-    p.pro_q = p.pro_k = p.pro_v = p.pro_b = nullptr;
-    if (pl.pro > 0) {  // q, k, v, beta after the prologue: behind the chunk blocks
-        const size_t el = a->dtype == KDA_BF16 ? 2 : 4;
-        auto al = [](size_t b) { return (b + 255) / 256 * 256; };
-        char *pb = ws + pl.table + pl.blocks;
-        const size_t nk = al((size_t)pl.rows * a->H * a->Dk * el), nv = al((size_t)pl.rows * a->H * a->Dv * el);
-        p.pro_q = pb;
-        p.pro_k = pb + nk;
-        p.pro_v = pb + 2 * nk;
-        p.pro_b = pb + 2 * nk + nv;
-    }
     const hipError_t e = kda::launch_chunk_fwd(a->dtype == KDA_BF16, a->Dk, a->Dv, p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     g_err[0] = 0;

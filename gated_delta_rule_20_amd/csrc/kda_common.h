@@ -162,6 +162,23 @@ __device__ __forceinline__ float rsq_norm(float x) {
     return __builtin_amdgcn_rsqf(fmaxf(x, 1.17549435e-38f));
 }
 
+// The sum over the 64 lanes of a wave, returned uniform, from DPP steps
+// (pairs, quads, 8- and 16-lane rows, then row broadcasts into rows 1-3; lane
+// 63 ends with the total) instead of LDS permutes.  All 64 lanes must be active.
+template <int CTRL, int ROWS> __device__ __forceinline__ float dpp_add(float v)
+{
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);  // row_mirror: every lane holds its 16-lane row's sum
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
 __device__ __forceinline__ float clamp_logdecay(float g, float g_min) {
     return fminf(fmaxf(g, g_min), 0.0f);
 }

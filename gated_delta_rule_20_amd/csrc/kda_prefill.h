@@ -39,17 +39,7 @@ struct PrefillParams {
     float *ckpt;                        // [N, ckpt_slots, H, Dk, Dv] or null
     int ckpt_every, ckpt_slots;         // chunks between checkpoints, slots per sequence
     FusionParams f;
-    void *pro_q, *pro_k, *pro_v, *pro_b;  // prologue outputs [rows, H, D] / [rows, H] (workspace)
 };
-
-// Bytes of the prologue's outputs (q, k, v, beta for every token, each array
-// 256-byte aligned) for `rows` tokens; 0 without the prologue.
-inline size_t prologue_bytes(int pro, long long rows, int H, int Dk, int Dv, int el)
-{
-    if (!pro) return 0;
-    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
-    return 2 * al((size_t)rows * H * Dk * el) + al((size_t)rows * H * Dv * el) + al((size_t)rows * H * el);
-}
 
 // Bytes of one (head, chunk) workspace block; 0 if the combination is unsupported.
 size_t block_bytes(int bf16, int Dk, int Dv);

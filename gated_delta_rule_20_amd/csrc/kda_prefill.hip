@@ -277,6 +277,77 @@ template <typename V> __device__ __forceinline__ void buf_store(__amdgpu_buffer_
     }
 }
 
+// With the layer prologue folded into the intra-chunk stage: the 3 projection
+// rows before the wave's 8 tokens (for its convolution) and the filter taps of
+// this lane's query, key and value channels, loaded one item ahead like RawIn.
+template <typename T, int DK, int DV> struct ProIn {
+    static constexpr int CPT = DK / 64, CPV = DV / 64;
+    typedef typename Vec<T, CPT>::type ku;
+    typedef typename Vec<T, CPV>::type vu;
+    ku hq[3], hk[3];
+    vu hv[3];
+    float wq[CPT][4], wk[CPT][4], wv[CPV][4];  // taps newest last, zero-padded at the old end
+};
+
+// History rows of tokens tb - 3 .. tb - 1 of a chunk: the tokens before (same
+// sequence), or at a sequence start the carried convolution state's rows
+// (slot i = state row i - 4 + W; older slots, or no state, read as zeros past
+// the descriptors' record counts).  lc: chunk index in its sequence, sq: the
+// sequence.
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void load_hist(ProIn<T, DK, DV> &pr, const PrefillParams &p, int tok0, int len, int sq,
+                                          int lc, int h, int tb, int l)
+{
+    using P = ProIn<T, DK, DV>;
+    constexpr int C = 2 * DK + DV, EL = (int)sizeof(T), CPT = P::CPT, CPV = P::CPV;
+    const int W = p.f.conv_w, rowk = p.H * DK * EL, rowv = p.H * DV * EL;
+    const bool tok_hist = tb > 0 || lc > 0;
+    // token rows tb - 3 + i exist for tb - 3 + i < len (rows before the chunk
+    // belong to the previous chunk of the sequence); the record counts end at
+    // the last of them, so a wave past the chunk's tokens reads nothing
+    const int nh = tok_hist ? min(max(len - (tb - 3), 0), 3) : 0;
+    const T *cs = (const T *)p.f.conv_state;
+    const bool st = !tok_hist && cs && W > 1;
+    const size_t rh = tok_hist ? (size_t)(tok0 + tb - 3) * p.H + h : 0;
+    const T *sb = st ? cs + ((size_t)sq * p.H + h) * (W - 1) * C : nullptr;
+    const int rk = nh ? (nh - 1) * rowk + DK * EL : 0, rv = nh ? (nh - 1) * rowv + DV * EL : 0;
+    const __amdgpu_buffer_rsrc_t dq = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(st ? sb : (const T *)p.q + rh * DK), 0, st ? (W - 1) * C * EL : rk, 0x00020000);
+    const __amdgpu_buffer_rsrc_t dk = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(st ? sb + DK : (const T *)p.k + rh * DK), 0, st ? (W - 1) * C * EL - DK * EL : rk, 0x00020000);
+    const __amdgpu_buffer_rsrc_t dv = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(st ? sb + 2 * DK : (const T *)p.v + rh * DV), 0, st ? (W - 1) * C * EL - 2 * DK * EL : rv, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int j = i - 4 + W;
+        const int sk = st ? (j >= 0 ? j * C * EL : 0x40000000) : i * rowk;  // row offset, per descriptor
+        const int sv = st ? (j >= 0 ? j * C * EL : 0x40000000) : i * rowv;
+        pr.hq[i] = buf_load<typename P::ku>(dq, sk + CPT * l * EL);
+        pr.hk[i] = buf_load<typename P::ku>(dk, sk + CPT * l * EL);
+        pr.hv[i] = buf_load<typename P::vu>(dv, sv + CPV * l * EL);
+    }
+}
+
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void load_taps(ProIn<T, DK, DV> &pr, const PrefillParams &p, int h, int l)
+{
+    using P = ProIn<T, DK, DV>;
+    constexpr int C = 2 * DK + DV;
+    const int W = p.f.conv_w;
+    const float *wb = p.f.conv_weight + (size_t)h * C * W;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int xw = e - 4 + W;
+#pragma unroll
+        for (int cc = 0; cc < P::CPT; ++cc) {
+            pr.wq[cc][e] = xw >= 0 ? wb[(P::CPT * l + cc) * W + xw] : 0.f;
+            pr.wk[cc][e] = xw >= 0 ? wb[(DK + P::CPT * l + cc) * W + xw] : 0.f;
+        }
+#pragma unroll
+        for (int cv = 0; cv < P::CPV; ++cv) pr.wv[cv][e] = xw >= 0 ? wb[(2 * DK + P::CPV * l + cv) * W + xw] : 0.f;
+    }
+}
+
 // Token range of chunk c; false if c is past the last chunk (packed tail).
 __device__ __forceinline__ bool locate_chunk(const PrefillParams &p, int c, int &tok0, int &len)
 {
@@ -339,9 +410,28 @@ __device__ __forceinline__ bool next_item(const PrefillParams &p, int &i, int &c
     return false;
 }
 
+// As next_item, with the item's sequence, its chunk index in the sequence and
+// the sequence length (the folded prologue needs them).
+__device__ __forceinline__ bool next_item_seq(const PrefillParams &p, int &i, int &c, int &h, int &tok0, int &len,
+                                              int &sq, int &lc, int &slen)
+{
+    const int n_items = p.n_chunks_cap * p.H;
+    for (; i < n_items; i += gridDim.x) {
+        const int ci = i / p.H;
+        h = i - ci * p.H;
+        c = p.n_chunks_cap - 1 - ci;
+        if (locate_seq(p, c, tok0, len, sq, lc, slen)) return true;
+    }
+    return false;
+}
+
 // ZM: decay logits z with the eq. (5) gate (A_log given), else log-decays g;
 // a template parameter so the elementwise pass carries no per-element branch.
-template <typename T, int DK, int DV, bool ZM>
+// PRO: the layer prologue (eq. (2)) folded in: q, k, v and beta hold the
+// projections before the convolution and the beta logits; P1a convolves,
+// applies Swish, L2Norm (q, k) and Sigmoid (beta) in registers, and writes the
+// convolution state and its checkpoints from the chunks that hold them.
+template <typename T, int DK, int DV, bool ZM, bool PRO = false>
 __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 {
     using BL = Block<T, DK, DV>;
@@ -358,11 +448,97 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
     const int ch0 = CPT * l;  // first channel of this lane in the elementwise phase
     const int m0 = w & 3, hf = w >> 2, tb = seg_base(w);  // elementwise: tile, half, first token
 
-    int i = blockIdx.x, c, h, tok0, len;
-    bool have = next_item(p, i, c, h, tok0, len);
+    using PI = ProIn<T, DK, DV>;
+    typedef typename PI::vu vu;
+    int i = blockIdx.x, c, h, tok0, len, sq = 0, lc = 0, slen = 0;
+    bool have = PRO ? next_item_seq(p, i, c, h, tok0, len, sq, lc, slen) : next_item(p, i, c, h, tok0, len);
     R raw;
+    PI pro;
     if (have) load_raw(raw, p, tok0, len, h, w, l);
+    if constexpr (PRO) {
+        if (have) {
+            load_hist(pro, p, tok0, len, sq, lc, h, tb, l);
+            load_taps(pro, p, h, l);
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0);
+    // The layer prologue of one item in registers (PRO): its convolution state and
+    // checkpoint rows from the pre-activations, then ShortConv, Swish and L2Norm
+    // into raw.q / raw.k / raw.v.  It runs for the first item before the loop and
+    // for each next item in the current item's P3, once the next item's loads
+    // have been waited for, where its VALU work fills the substitution's MFMA
+    // latency.
+    auto prologue_regs = [&](int len, int sq, int lc, int slen, int h) {
+            constexpr int C = 2 * DK + DV;
+            const int W = p.f.conv_w;
+            // Convolution state: the pre-activations of chunk positions q0 .. q0 + W - 2,
+            // written by the wave whose rows hold them (row e holds position tb - 3 + e).
+            auto put_rows = [&](T *dst, int q0) {
+#pragma unroll
+                for (int e = 0; e < 3 + HT; ++e) {
+                    const int j = tb - 3 + e - q0;  // its state row
+                    if (j < 0 || j >= W - 1 || (e < 3 && tb - 3 + e >= 0)) continue;  // not kept, or another wave's token
+                    *reinterpret_cast<ku *>(dst + (size_t)j * C + CPT * l) = e < 3 ? pro.hq[e] : raw.q[e - 3];
+                    *reinterpret_cast<ku *>(dst + (size_t)j * C + DK + CPT * l) = e < 3 ? pro.hk[e] : raw.k[e - 3];
+                    *reinterpret_cast<vu *>(dst + (size_t)j * C + 2 * DK + CPV * l) = e < 3 ? pro.hv[e] : raw.v[e - 3];
+                }
+            };
+            if (W > 1 && p.f.conv_state_out && lc * CHUNK + len == slen)
+                put_rows((T *)p.f.conv_state_out + ((size_t)sq * p.H + h) * (W - 1) * C, len - (W - 1));
+            if (W > 1 && p.f.conv_ckpt && p.ckpt_every > 0 && (lc + 1) % p.ckpt_every == 0) {
+                const int slot = (lc + 1) / p.ckpt_every - 1;
+                if (slot < p.ckpt_slots && (lc + 1) * CHUNK < slen)
+                    put_rows((T *)p.f.conv_ckpt + (((size_t)sq * p.ckpt_slots + slot) * p.H + h) * (W - 1) * C,
+                             CHUNK - (W - 1));
+            }
+            // ShortConv (taps zero-padded to width 4), Swish, and for q and k L2Norm
+            // over the head's channels (this wave holds all of them for its tokens).
+            // Tokens run last to first, so each token's own row is replaced by its
+            // result only after the later tokens that read it as history.
+            auto swish = [](float u) { return u * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-LOG2E * u)); };
+#pragma unroll
+            for (int r = HT - 1; r >= 0; --r) {
+                float aq[CPT], ak[CPT], sq2_ = 0.f, sk2_ = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    float cq = 0.f, ck = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = r + e;  // 0..2: history, 3..: tokens
+                        cq += pro.wq[cc][e] * to_f<T>((row < 3 ? pro.hq[row] : raw.q[row - 3])[cc]);
+                        ck += pro.wk[cc][e] * to_f<T>((row < 3 ? pro.hk[row] : raw.k[row - 3])[cc]);
+                    }
+                    aq[cc] = swish(cq);
+                    ak[cc] = swish(ck);
+                    sq2_ += aq[cc] * aq[cc];
+                    sk2_ += ak[cc] * ak[cc];
+                }
+                float av[CPV];
+#pragma unroll
+                for (int cv = 0; cv < CPV; ++cv) {
+                    float cx = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = r + e;
+                        cx += pro.wv[cv][e] * to_f<T>((row < 3 ? pro.hv[row] : raw.v[row - 3])[cv]);
+                    }
+                    av[cv] = swish(cx);
+                }
+                const bool ok = tb + r < len;  // padded tokens carry q = k = v = 0
+                const float nq = rsq_norm(wave_sum(sq2_) + p.f.qk_eps);
+                const float nk = rsq_norm(wave_sum(sk2_) + p.f.qk_eps);
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    raw.q[r][cc] = from_f<T>(ok ? aq[cc] * nq : 0.f);
+                    raw.k[r][cc] = from_f<T>(ok ? ak[cc] * nk : 0.f);
+                }
+#pragma unroll
+                for (int cv = 0; cv < CPV; ++cv) raw.v[r][cv] = from_f<T>(ok ? av[cv] : 0.f);
+            }
+    };
+    if constexpr (PRO) {
+        if (have) prologue_regs(len, sq, lc, slen, h);
+    }
 
     while (have) {
         char *blkb = p.blocks + ((size_t)h * p.n_chunks_cap + c) * BL::BYTES;
@@ -375,8 +551,9 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         // wait here holds back on the previous item's result stores.
         // The next item's raw inputs are loaded into each raw register right after
         // its last use below, so the loads issue between this item's VALU work.
-        int i2 = i + gridDim.x, c2 = 0, h2 = 0, tok2 = 0, len2 = 0;
-        const bool have2 = next_item(p, i2, c2, h2, tok2, len2);
+        int i2 = i + gridDim.x, c2 = 0, h2 = 0, tok2 = 0, len2 = 0, sq2 = 0, lc2 = 0, slen2 = 0;
+        const bool have2 = PRO ? next_item_seq(p, i2, c2, h2, tok2, len2, sq2, lc2, slen2)
+                               : next_item(p, i2, c2, h2, tok2, len2);
         // The next item's rows of this wave through buffer descriptors: base at its
         // first token (uniform), lane offset plus token offset in one VGPR shared by
         // g, k and q, and a record count that ends at the last valid token, so tokens
@@ -412,7 +589,19 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             }
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) sm.tot[2 * m0 + hf][ch0 + cc] = run[cc];
-            if (l < HT) sm.beta[tb + l] = to_f<T>(raw.beta);
+            if constexpr (PRO) {  // Sigmoid of the logit; padded tokens keep beta = 0
+                if (l < HT) sm.beta[tb + l] = (tb + l < len) ? __builtin_amdgcn_rcpf(1.f + __expf(-to_f<T>(raw.beta))) : 0.f;
+            } else {
+                if (l < HT) sm.beta[tb + l] = to_f<T>(raw.beta);
+            }
+        }
+        if constexpr (PRO) {
+            // the next item's history rows and (for another head) taps, after their
+            // last use (the next item's prologue ran in the previous item's P3)
+            if (have2) {
+                load_hist(pro, p, tok2, len2, sq2, lc2, h2, tb, l);
+                if (h2 != h) load_taps(pro, p, h2, l);
+            }
         }
         {
             const int bt = tb + l;
@@ -699,6 +888,9 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 }
                 for (int f = 2 * KS + w - 3; f < 4 * KS; f += IWAVES - 3) qp_frag(f);  // second half of Q+
             }
+            if constexpr (PRO) {
+                if (have2) prologue_regs(len2, sq2, lc2, slen2, h2);
+            }
         }
         lds_barrier();
 
@@ -739,6 +931,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         }
         lds_barrier();  // LDS is reused by the next item
         i = i2; c = c2; h = h2; tok0 = tok2; len = len2;
+        sq = sq2; lc = lc2; slen = slen2;
         have = have2;
     }
 }
@@ -1224,206 +1417,6 @@ __global__ __launch_bounds__(256) void chain_wide_kernel(PrefillParams p)
 }
 
 // -----------------------------------------------------------------------------
-// Layer prologue (eq. (2)) as a pass of its own ahead of the intra-chunk stage.
-// (Folded into the intra-chunk kernel's elementwise phase it pushed that kernel
-// past its register budget: spills on the prefetched inputs serialised their
-// loads and tripled its time.)  One workgroup per (chunk, head); wave w takes
-// tokens 16 w .. 16 w + 15 of the chunk, lane l the query and key channels
-// CPT*l.. and the value channels CPV*l.., and reads 19 rows of each projection
-// (the 16 tokens and the 3 before them: the previous chunk of the same
-// sequence, or conv_state at a sequence start).  Per token and channel:
-// ShortConv (taps zero-padded to width 4), Swish, and for q and k L2Norm over
-// the head's channels (one 16-value wave reduction per 8 tokens: their 8 key
-// and 8 query norms); Sigmoid of the beta logit.  bf16 q, k, v, beta go to the workspace, where the intra-chunk stage
-// reads them in place of its inputs.  The last chunk of a sequence also writes
-// the convolution state, a checkpoint chunk its convolution checkpoint.
-
-// Sums each of 16 per-lane values over the wave's 64 lanes (a transposed
-// butterfly: each exchange halves the values a lane carries, 17 lane swaps in
-// all instead of 96); every lane receives the 16 totals.
-__device__ __forceinline__ void wave_sum16(const float (&v)[16], float (&out)[16], int l)
-{
-    float a[8], b[4], c[2];
-    const bool b5 = l & 32, b4 = l & 16, b3 = l & 8, b2 = l & 4;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = (b5 ? v[i + 8] : v[i]) + __shfl_xor(b5 ? v[i] : v[i + 8], 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = (b4 ? a[i + 4] : a[i]) + __shfl_xor(b4 ? a[i] : a[i + 4], 16);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) c[i] = (b3 ? b[i + 2] : b[i]) + __shfl_xor(b3 ? b[i] : b[i + 2], 8);
-    float d = (b2 ? c[1] : c[0]) + __shfl_xor(b2 ? c[0] : c[1], 4);  // value 8 b5 + 4 b4 + 2 b3 + b2
-    d += __shfl_xor(d, 2);
-    d += __shfl_xor(d, 1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) out[i] = __shfl(d, 4 * i);
-}
-
-template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void prologue_kernel(PrefillParams p)
-{
-    constexpr int C = 2 * DK + DV, CPT = DK / 64, CPV = DV / 64, TW = 16, NR = TW + 3, HW = 8;
-    constexpr int EL = (int)sizeof(T);
-    typedef typename Vec<T, CPT>::type ku;
-    typedef typename Vec<T, CPV>::type vu;
-    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = blockIdx.x, h = blockIdx.y;
-    int tok0, len, sq, lc, slen;
-    if (!locate_seq(p, c, tok0, len, sq, lc, slen)) return;
-    const int tb = TW * w;
-    if (tb >= len) return;
-    const int W = p.f.conv_w;
-    const int rowk = p.H * DK * EL, rowv = p.H * DV * EL;
-
-    // rows 0..2: positions tb - 3 .. tb - 1; rows 3..18: the wave's tokens (zero past the chunk)
-    ku xq[NR], xk[NR];
-    vu xv[NR];
-    {
-        // All 19 rows are requested before any is used: the 3 history rows through
-        // one descriptor over either the 3 tokens before (same sequence) or this
-        // sequence's conv_state rows (slot i = row i - 4 + W; older slots, or no
-        // conv_state, read past the record count and give zeros).
-        const bool tok_hist = tb > 0 || lc > 0;
-        const T *cs = (const T *)p.f.conv_state;
-        const bool st = !tok_hist && cs && W > 1;
-        const size_t rh = tok_hist ? (size_t)(tok0 + tb - 3) * p.H + h : 0;
-        const __amdgpu_buffer_rsrc_t hq = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(st ? cs + ((size_t)sq * p.H + h) * (W - 1) * C : (const T *)p.q + rh * DK), 0,
-            st ? (W - 1) * C * EL : (tok_hist ? 2 * rowk + DK * EL : 0), 0x00020000);
-        const __amdgpu_buffer_rsrc_t hk = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(st ? cs + ((size_t)sq * p.H + h) * (W - 1) * C + DK : (const T *)p.k + rh * DK), 0,
-            st ? (W - 1) * C * EL - DK * EL : (tok_hist ? 2 * rowk + DK * EL : 0), 0x00020000);
-        const __amdgpu_buffer_rsrc_t hv = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(st ? cs + ((size_t)sq * p.H + h) * (W - 1) * C + 2 * DK : (const T *)p.v + rh * DV), 0,
-            st ? (W - 1) * C * EL - 2 * DK * EL : (tok_hist ? 2 * rowv + DV * EL : 0), 0x00020000);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            const int j = i - 4 + W;
-            const int sk = st ? (j >= 0 ? j * C * EL : 0x40000000) : i * rowk;  // row offset, per descriptor
-            const int sv = st ? (j >= 0 ? j * C * EL : 0x40000000) : i * rowv;
-            xq[i] = buf_load<ku>(hq, sk + CPT * l * EL);
-            xk[i] = buf_load<ku>(hk, sk + CPT * l * EL);
-            xv[i] = buf_load<vu>(hv, sv + CPV * l * EL);
-        }
-        const int nv = min(len - tb, TW);
-        const size_t r0 = (size_t)(tok0 + tb) * p.H + h;
-        const int rk = (nv - 1) * rowk + DK * EL, rv = (nv - 1) * rowv + DV * EL;
-        const __amdgpu_buffer_rsrc_t dq = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.q + r0 * DK), 0, rk, 0x00020000);
-        const __amdgpu_buffer_rsrc_t dk = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.k + r0 * DK), 0, rk, 0x00020000);
-        const __amdgpu_buffer_rsrc_t dv = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.v + r0 * DV), 0, rv, 0x00020000);
-#pragma unroll
-        for (int r = 0; r < TW; ++r) {
-            xq[3 + r] = buf_load<ku>(dq, r * rowk + CPT * l * EL);
-            xk[3 + r] = buf_load<ku>(dk, r * rowk + CPT * l * EL);
-            xv[3 + r] = buf_load<vu>(dv, r * rowv + CPV * l * EL);
-        }
-    }
-    const float *wb = p.f.conv_weight + (size_t)h * C * W;
-    auto taps = [&](int chan, float (&t4)[4]) {  // newest last, zero-padded at the old end
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int xw = e - 4 + W;
-            t4[e] = xw >= 0 ? wb[chan * W + xw] : 0.f;
-        }
-    };
-    auto swish = [](float u) { return u * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-LOG2E * u)); };
-
-    // Outputs through descriptors whose record count ends at the chunk's last
-    // token: stores past it are dropped, so no per-token branch is needed.
-    const int nv = min(len - tb, TW);
-    const size_t r0 = (size_t)(tok0 + tb) * p.H + h;
-    const int rk = (nv - 1) * rowk + DK * EL, rv = (nv - 1) * rowv + DV * EL;
-    const __amdgpu_buffer_rsrc_t oq = __builtin_amdgcn_make_buffer_rsrc((void *)((T *)p.pro_q + r0 * DK), 0, rk, 0x00020000);
-    const __amdgpu_buffer_rsrc_t ok_ = __builtin_amdgcn_make_buffer_rsrc((void *)((T *)p.pro_k + r0 * DK), 0, rk, 0x00020000);
-    // q and k, in two halves of 8 tokens: convolve, Swish, then L2Norm with the
-    // half's 8 key and 8 query sums of squares in one 16-value reduction
-    float tq[CPT][4], tk[CPT][4];
-#pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) {
-        taps(CPT * l + cc, tq[cc]);
-        taps(DK + CPT * l + cc, tk[cc]);
-    }
-#pragma unroll
-    for (int hb = 0; hb < TW; hb += HW) {
-        float a[2][HW][CPT], ss[2 * HW];
-#pragma unroll
-        for (int sidx = 0; sidx < 2; ++sidx) {  // 0: keys, 1: queries
-#pragma unroll
-            for (int r = 0; r < HW; ++r) {
-                ss[sidx * HW + r] = 0.f;
-#pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) {
-                    float cx = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        cx += (sidx ? tq : tk)[cc][e] * to_f<T>((sidx ? xq[hb + r + e] : xk[hb + r + e])[cc]);
-                    a[sidx][r][cc] = swish(cx);
-                    ss[sidx * HW + r] += a[sidx][r][cc] * a[sidx][r][cc];
-                }
-            }
-        }
-        float tot[2 * HW];
-        wave_sum16(ss, tot, l);
-#pragma unroll
-        for (int sidx = 0; sidx < 2; ++sidx) {
-#pragma unroll
-            for (int r = 0; r < HW; ++r) {
-                const float n = rsq_norm(tot[sidx * HW + r] + p.f.qk_eps);
-                ku o;
-#pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) o[cc] = from_f<T>(a[sidx][r][cc] * n);
-                buf_store<ku>(sidx ? oq : ok_, (hb + r) * rowk + CPT * l * EL, o);
-            }
-        }
-    }
-    {   // v: convolve, Swish, store
-        float t4[CPV][4];
-#pragma unroll
-        for (int cv = 0; cv < CPV; ++cv) taps(2 * DK + CPV * l + cv, t4[cv]);
-        const __amdgpu_buffer_rsrc_t od = __builtin_amdgcn_make_buffer_rsrc((void *)((T *)p.pro_v + r0 * DV), 0, rv, 0x00020000);
-#pragma unroll
-        for (int r = 0; r < TW; ++r) {
-            vu o;
-#pragma unroll
-            for (int cv = 0; cv < CPV; ++cv) {
-                float cx = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) cx += t4[cv][e] * to_f<T>(xv[r + e][cv]);
-                o[cv] = from_f<T>(swish(cx));
-            }
-            buf_store<vu>(od, r * rowv + CPV * l * EL, o);
-        }
-    }
-    {   // beta = Sigmoid(logit), lanes 0..15
-        const int rb = (nv - 1) * p.H * EL + EL;
-        const __amdgpu_buffer_rsrc_t ib = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.beta + r0), 0, rb, 0x00020000);
-        const __amdgpu_buffer_rsrc_t ob = __builtin_amdgcn_make_buffer_rsrc((void *)((T *)p.pro_b + r0), 0, rb, 0x00020000);
-        const int off = l < TW ? l * p.H * EL : 0x40000000;  // lanes past the wave's tokens: past the record count, nothing read or written
-        const T b = buf_load<T>(ib, off);
-        buf_store<T>(ob, off, from_f<T>(1.f / (1.f + __expf(-to_f<T>(b)))));
-    }
-    // Convolution state: the pre-activations of chunk positions q0 .. q0 + W - 2,
-    // taken by the wave whose rows hold them (position q is row q - tb + 3).
-    auto put_rows = [&](T *dst, int q0) {
-#pragma unroll
-        for (int e = 0; e < NR; ++e) {  // row e holds chunk position tb - 3 + e
-            const int j = tb - 3 + e - q0;  // its state row
-            if (j < 0 || j >= W - 1 || (e < 3 && tb - 3 + e >= 0)) continue;  // not kept, or another wave's token
-            *reinterpret_cast<ku *>(dst + (size_t)j * C + CPT * l) = xq[e];
-            *reinterpret_cast<ku *>(dst + (size_t)j * C + DK + CPT * l) = xk[e];
-            *reinterpret_cast<vu *>(dst + (size_t)j * C + 2 * DK + CPV * l) = xv[e];
-        }
-    };
-    if (W > 1 && p.f.conv_state_out && lc * CHUNK + len == slen)
-        put_rows((T *)p.f.conv_state_out + ((size_t)sq * p.H + h) * (W - 1) * C, len - (W - 1));
-    if (W > 1 && p.f.conv_ckpt && p.ckpt_every > 0 && (lc + 1) % p.ckpt_every == 0) {
-        const int slot = (lc + 1) / p.ckpt_every - 1;
-        if (slot < p.ckpt_slots && (lc + 1) * CHUNK < slen)
-            put_rows((T *)p.f.conv_ckpt + (((size_t)sq * p.ckpt_slots + slot) * p.H + h) * (W - 1) * C,
-                     CHUNK - (W - 1));
-    }
-}
-
-// -----------------------------------------------------------------------------
 // Output epilogue (eq. (6) without W_o), in place on o after the chain:
 // o <- Sigmoid(gate) * w_h * o / sqrt(mean(o^2) + eps) per (token, head) row.
 // The chain holds 16 of a head's d_v columns per workgroup, so the per-row
@@ -1495,28 +1488,31 @@ static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
     if (p.varlen)
         hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(table::THREADS), 0, st, p.cu, p.N, p.T, p.n_chunks_cap,
                            p.chunk_off, p.order, p.span);
-    const bool pro = p.f.conv_w > 0;
-    if (pro && p.n_chunks_cap > 0)
-        hipLaunchKernelGGL((prologue_kernel<T, DK, DV>), dim3((unsigned)p.n_chunks_cap, (unsigned)p.H), dim3(256), 0, st, p);
-    PrefillParams pi = p;  // with the prologue, the intra-chunk stage reads its outputs
-    if (pro) {
-        pi.q = p.pro_q; pi.k = p.pro_k; pi.v = p.pro_v; pi.beta = p.pro_b;
-    }
+    const bool pro = p.f.conv_w > 0;  // the prologue runs inside the intra-chunk stage
     if (p.n_chunks_cap > 0) {
         const size_t smem = sizeof(IntraSmem<T, DK, DV>);
         static_assert(sizeof(IntraSmem<T, DK, DV>) <= 160 * 1024, "intra-chunk LDS exceeds 160 KiB");
-        static const hipError_t attr_z = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, true>,
-                                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        static const hipError_t attr_g = hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, false>,
-                                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (attr_z != hipSuccess) return attr_z;
-        if (attr_g != hipSuccess) return attr_g;
+        static const hipError_t attr[4] = {
+            hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, true, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem),
+            hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, false, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem),
+            hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, true, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem),
+            hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, false, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem)};
+        for (hipError_t e : attr)
+            if (e != hipSuccess) return e;
         const long items = (long)p.n_chunks_cap * p.H;
         const unsigned grid = (unsigned)(items < intra_grid() ? items : intra_grid());
-        if (p.A_log)
-            hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, true>), dim3(grid), dim3(64 * IWAVES), smem, st, pi);
-        else
-            hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, false>), dim3(grid), dim3(64 * IWAVES), smem, st, pi);
+        const dim3 gd(grid), bd(64 * IWAVES);
+        if (p.A_log) {
+            if (pro) hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, true, true>), gd, bd, smem, st, p);
+            else hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, true, false>), gd, bd, smem, st, p);
+        } else {
+            if (pro) hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, false, true>), gd, bd, smem, st, p);
+            else hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, false, false>), gd, bd, smem, st, p);
+        }
     }
     const long npairs = (long)p.N * p.H;
     if (npairs >= WIDE_CHAIN_PAIRS) {

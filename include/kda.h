@@ -188,10 +188,9 @@ typedef struct {
     const kda_layer_fusion_t *fusion;   /* optional prologue / epilogue, or NULL */
 } kda_chunk_fwd_args_t;
 
-/* Workspace bytes kda_chunk_fwd needs for these shapes (pointers are not read,
- * except that a fusion struct with conv_width > 0 adds room for the prologue's
- * q, k, v, beta).  Depends on B, T, H, Dk, Dv, dtype, on whether cu_seqlens is
- * set (and N) and on whether the prologue is on. */
+/* Workspace bytes kda_chunk_fwd needs for these shapes (pointers are not
+ * read).  Depends on B, T, H, Dk, Dv, dtype and on whether cu_seqlens is set
+ * (and N); the layer prologue and epilogue need none. */
 KDA_API kda_status_t kda_chunk_fwd_workspace_size(const kda_chunk_fwd_args_t *args, size_t *bytes);
 
 KDA_API kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *args, void *stream);
@@ -206,7 +205,7 @@ KDA_API kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *args, void *strea
  * process ends.  args->workspace must be NULL and args->workspace_bytes 0.
  * Shapes whose kda_chunk_fwd_workspace_size exceeds the array are rejected
  * with KDA_ERROR_WORKSPACE before anything is enqueued (at bf16 and
- * Dk = Dv = 128 without the prologue the array holds 897 chunk blocks of
+ * Dk = Dv = 128 the array holds 897 chunk blocks of
  * 64 tokens x 1 head, e.g. B = 1, T = 7168 tokens at H = 8).  The array used
  * is the copy on the device that is current when the call is made, which must
  * be the stream's device.  Every call on one device uses the same array, so

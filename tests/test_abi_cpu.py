@@ -323,18 +323,16 @@ def test_prefill_fusion_rejects_before_launch(lib):
     del ws
 
 
-def test_prologue_workspace_grows(lib):
-    """The fused prologue adds its convolved q, k, v, beta to the workspace:
-    rows*H*(2*Dk + Dv) + rows*H elements, each array 256-byte aligned."""
+def test_prologue_needs_no_workspace(lib):
+    """The layer prologue runs in the intra-chunk stage's registers: a fusion
+    struct with conv_width > 0 leaves the workspace size unchanged."""
     st, base = _ws(lib, _args())
     f = _fusion()
     a = _args()
     a.fusion = ctypes.pointer(f)
     out = ctypes.c_size_t(0)
-    assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(out)) == 0
-    rows, H = 128, 2
-    al = lambda b: (b + 255) // 256 * 256
-    assert out.value == base + 2 * al(rows * H * 128 * 2) + al(rows * H * 128 * 2) + al(rows * H * 2)
+    assert st == 0 and lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(out)) == 0
+    assert out.value == base
 
 
 def test_noalloc_limit_matches_header():

@@ -7,9 +7,9 @@ kernels on the same data, so they must agree bit for bit.  Calls follow one
 another on one device, largest first, so every call after the first runs on
 an array that still holds the previous call's blocks: packed sequences over
 128 (sequence, head) pairs (one workgroup per pair in the chain), then a
-smaller batched call with the layer prologue and epilogue fused (the
-prologue's q, k, v, beta sit behind the chunk blocks in the workspace), then
-a smaller float32 call.  A shape beyond the array is rejected and leaves the
+smaller batched call with the layer prologue and epilogue fused (its
+convolution state written by the intra-chunk stage), then a smaller float32
+call.  A shape beyond the array is rejected and leaves the
 output untouched."""
 import dataclasses
 
