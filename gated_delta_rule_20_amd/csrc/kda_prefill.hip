@@ -172,6 +172,7 @@ template <typename T, int DK, int DV> struct IntraSmem {
     float tot[8][DK];      // half-tile (8-token segment) totals (log2 units)
     float eB[4][DK];       // exp(B_m) per tile and channel (P1 -> P3)
     float beta[CHUNK];
+    float gam[DK];         // gamma^C of the chunk (pair mode: P1 -> chain step)
 };
 
 // Upper block of L that holds D_m = (I + L_mm)^-1: (0,1), (0,2), (0,3), (1,2).
@@ -410,6 +411,47 @@ __device__ __forceinline__ bool next_item(const PrefillParams &p, int &i, int &c
     return false;
 }
 
+// Pair mode: workgroup b takes the (sequence, head) pairs of rank b, b + G, ...
+// (G = gridDim.x; ranks in the chunk table's longest-first order) and walks
+// each pair's chunks in order.  pair_of: the pair of rank r; false past the last.
+__device__ __forceinline__ bool pair_of(const PrefillParams &p, int r, int &s, int &h, int &start, int &slen, int &nch)
+{
+    if (r >= p.N * p.H) return false;
+    const int srank = r / p.H;
+    h = r - srank * p.H;
+    if (p.varlen) {
+        s = ld_uniform(p.order, srank);
+        start = ld_uniform(p.span, 2 * s);
+        slen = ld_uniform(p.span, 2 * s + 1);
+        nch = ld_uniform(p.chunk_off, s + 1) - ld_uniform(p.chunk_off, s);
+    } else {
+        s = srank;
+        start = s * p.T;
+        slen = p.T;
+        nch = (p.T + CHUNK - 1) / CHUNK;
+    }
+    return true;
+}
+
+// The chunk after (r, lc): the pair's next chunk, else chunk 0 of this
+// workgroup's next pair that has chunks; its token range.  False when done.
+__device__ __forceinline__ bool pair_next(const PrefillParams &p, int &r, int &lc, int &s, int &h, int &start,
+                                          int &slen, int &nch, int &tok0, int &len)
+{
+    if (lc + 1 < nch) {
+        ++lc;
+    } else {
+        lc = 0;
+        for (r += gridDim.x;; r += gridDim.x) {
+            if (!pair_of(p, r, s, h, start, slen, nch)) return false;
+            if (nch > 0) break;
+        }
+    }
+    tok0 = start + lc * CHUNK;
+    len = min(CHUNK, slen - lc * CHUNK);
+    return true;
+}
+
 // As next_item, with the item's sequence, its chunk index in the sequence and
 // the sequence length (the folded prologue needs them).
 __device__ __forceinline__ bool next_item_seq(const PrefillParams &p, int &i, int &c, int &h, int &tok0, int &len,
@@ -431,7 +473,13 @@ __device__ __forceinline__ bool next_item_seq(const PrefillParams &p, int &i, in
 // projections before the convolution and the beta logits; P1a convolves,
 // applies Swish, L2Norm (q, k) and Sigmoid (beta) in registers, and writes the
 // convolution state and its checkpoints from the chunks that hold them.
-template <typename T, int DK, int DV, bool ZM, bool PRO = false>
+// PAIR: the chain runs in the same workgroup (pair mode, above): each chunk's
+// block goes to LDS regions the intra-chunk work no longer needs (Q+ over the
+// row operand KR, U over QR, W over L, A behind Tp, gamma^C in gam; K~^T is
+// read from KtT in place), and after P4 each wave advances one 16-column tile
+// of the pair's state by the chunk as the wide chain does (state columns in
+// MFMA accumulators).  No block crosses HBM.
+template <typename T, int DK, int DV, bool ZM, bool PRO = false, bool PAIR = false>
 __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 {
     using BL = Block<T, DK, DV>;
@@ -450,8 +498,28 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 
     using PI = ProIn<T, DK, DV>;
     typedef typename PI::vu vu;
-    int i = blockIdx.x, c, h, tok0, len, sq = 0, lc = 0, slen = 0;
-    bool have = PRO ? next_item_seq(p, i, c, h, tok0, len, sq, lc, slen) : next_item(p, i, c, h, tok0, len);
+    static_assert(!PAIR || (sizeof(T) == 2 && DK == 128 && !PRO), "pair mode: bf16, d_k = 128, no prologue");
+    // pair mode: wave w < NCW holds state column tile w (CT = 1), all NR row tiles
+    constexpr int CT = 1, NR = DK / 16, NCW = DV / 16;
+    static_assert(NCW <= IWAVES, "a chain wave per column tile");
+    int i = blockIdx.x, c = 0, h = 0, tok0 = 0, len = 0, sq = 0, lc = 0, slen = 0, pst = 0, nch = 0;
+    bool have;
+    f32x4 S[NR][CT];  // pair mode, waves w < NCW: the pair's state, columns 16 w + x
+    if constexpr (PAIR) {
+        // pairs without tokens: the final state is the initial one
+        for (int r = blockIdx.x;; r += gridDim.x) {
+            int s_, h_, st_, sl_, n_;
+            if (!pair_of(p, r, s_, h_, st_, sl_, n_)) break;
+            if (n_ == 0 && p.hT) {
+                const size_t sb = ((size_t)s_ * p.H + h_) * DK * DV;
+                for (int e = t; e < DK * DV; e += 64 * IWAVES) p.hT[sb + e] = p.h0 ? p.h0[sb + e] : 0.f;
+            }
+        }
+        i = (int)blockIdx.x - (int)gridDim.x;
+        have = pair_next(p, i, lc, sq, h, pst, slen, nch, tok0, len);
+    } else {
+        have = PRO ? next_item_seq(p, i, c, h, tok0, len, sq, lc, slen) : next_item(p, i, c, h, tok0, len);
+    }
     R raw;
     PI pro;
     if (have) load_raw(raw, p, tok0, len, h, w, l);
@@ -543,7 +611,36 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
     while (have) {
         char *blkb = p.blocks + ((size_t)h * p.n_chunks_cap + c) * BL::BYTES;
         T *blk = reinterpret_cast<T *>(blkb);
-        float *gamma_out = reinterpret_cast<float *>(blkb + BL::GAMMA_BYTE);
+        // where this chunk's block goes: the workspace, or (pair mode) LDS
+        T *bW, *bQ, *bA, *bU;
+        float *bG;
+        if constexpr (PAIR) {
+            bW = reinterpret_cast<T *>(&sm.L[0][0]);
+            bQ = &sm.ops.KR[0][0];
+            bU = &sm.ops.QR[0][0];
+            bA = reinterpret_cast<T *>(reinterpret_cast<char *>(&sm.y.t.Tp[0][0]) + sizeof(sm.y.t.Tp));
+            bG = sm.gam;
+            static_assert(!PAIR || (sizeof(sm.L) >= 16 * 1024 && sizeof(sm.ops.KR) >= 16 * 1024 &&
+                                    sizeof(sm.ops.QR) >= 16 * 1024 &&
+                                    offsetof(SM, y.t.Tp) + sizeof(sm.y.t.Tp) + 8 * 1024 <= offsetof(SM, y) + sizeof(sm.y)),
+                          "pair mode: LDS regions for the block");
+            if (lc == 0 && w < NCW) {  // the pair's entering state (waited for in P3)
+                const size_t sb = ((size_t)sq * p.H + h) * DK * DV;
+#pragma unroll
+                for (int R = 0; R < NR; ++R)
+#pragma unroll
+                    for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            S[R][cc][e] = p.h0 ? p.h0[sb + (size_t)(16 * R + 4 * g + e) * DV + 16 * (CT * w + cc) + x] : 0.f;
+            }
+        } else {
+            bW = blk + BL::W_OFF;
+            bQ = blk + BL::Q_OFF;
+            bU = blk + BL::U_OFF;
+            bA = blk + BL::A_OFF;
+            bG = reinterpret_cast<float *>(blkb + BL::GAMMA_BYTE);
+        }
 
         // ---- P1: gate (eq. 5), in-tile cumsum, elementwise operands ----------
         // The raw registers were loaded during the previous item (or before the
@@ -551,9 +648,14 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         // wait here holds back on the previous item's result stores.
         // The next item's raw inputs are loaded into each raw register right after
         // its last use below, so the loads issue between this item's VALU work.
-        int i2 = i + gridDim.x, c2 = 0, h2 = 0, tok2 = 0, len2 = 0, sq2 = 0, lc2 = 0, slen2 = 0;
-        const bool have2 = PRO ? next_item_seq(p, i2, c2, h2, tok2, len2, sq2, lc2, slen2)
-                               : next_item(p, i2, c2, h2, tok2, len2);
+        int i2 = i + gridDim.x, c2 = 0, h2 = 0, tok2 = 0, len2 = 0, sq2 = 0, lc2 = 0, slen2 = 0, pst2 = 0, nch2 = 0;
+        bool have2;
+        if constexpr (PAIR) {
+            i2 = i; lc2 = lc; sq2 = sq; h2 = h; pst2 = pst; slen2 = slen; nch2 = nch;
+            have2 = pair_next(p, i2, lc2, sq2, h2, pst2, slen2, nch2, tok2, len2);
+        } else {
+            have2 = PRO ? next_item_seq(p, i2, c2, h2, tok2, len2, sq2, lc2, slen2) : next_item(p, i2, c2, h2, tok2, len2);
+        }
         // The next item's rows of this wave through buffer descriptors: base at its
         // first token (uniform), lane offset plus token offset in one VGPR shared by
         // g, k and q, and a record count that ends at the last valid token, so tokens
@@ -678,7 +780,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             }
             if (w == 0) {  // gamma^C, stored after the last use of the raw registers
 #pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) gamma_out[ch0 + cc] = gC[cc];
+                for (int cc = 0; cc < CPT; ++cc) bG[ch0 + cc] = gC[cc];
             }
 #pragma unroll
             for (int cv = 0; cv < CPV; ++cv) {
@@ -706,7 +808,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 qp[e] = from_f<T>(to_f<T>(qr[e]) * e0[e]);
                 qp[4 + e] = from_f<T>(to_f<T>(qr[4 + e]) * e1[e]);
             }
-            store8(blk + BL::Q_OFF + ((m * KS + ks) * 64 + l) * 8, qp);
+            store8(bQ + ((m * KS + ks) * 64 + l) * 8, qp);
         };
 
         // ---- P2: L and A sub-tiles on MFMA; diagonal inverses ----------------
@@ -732,6 +834,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         float(*L)[SM::LP] = sm.L;
         constexpr int LP = SM::LP;
         f32x4 dmv = {0.f, 0.f, 0.f, 0.f};  // waves 0-3: D_w in accumulator layout, D[4g+i][x]
+        f32x4 apend0 = {0.f, 0.f, 0.f, 0.f}, apend1 = {0.f, 0.f, 0.f, 0.f};  // pair mode: A tiles for P3
         {
             auto pair_products = [&](int m, int n, bool doL, bool doA, f32x4 &aL, f32x4 &aA) {
                 const int cr = colop_row(m, n);
@@ -762,18 +865,24 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 for (int ii = 0; ii < 4; ++ii) v[ii] = (m != n || x < 4 * g + ii) ? bt[ii] * aL[ii] : 0.f;
                 return v;
             };
-            auto store_a = [&](int m, int n, const f32x4 &aA) {
+            // A tiles go to the workspace at once; in pair mode their LDS region is
+            // still being read here, so they wait in registers for P3 (slot 0: the
+            // wave's first pair, slot 1: the A half of (3,1) or (3,2)).
+            auto store_a = [&](int m, int n, const f32x4 &aA, int slot) {
                 f32x4 a4;
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) a4[ii] = (m != n || 4 * g + ii <= x) ? aA[ii] : 0.f;
-                *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
-                    make_quad<T>(a4);
+                if constexpr (PAIR) {
+                    (slot == 0 ? apend0 : apend1) = a4;
+                } else {
+                    *reinterpret_cast<quad_t<T> *>(bA + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) = make_quad<T>(a4);
+                }
             };
             f32x4 aL, aA;
             if (w < 4) {
                 const int m = w, o0 = 16 * w;
                 pair_products(m, m, true, true, aL, aA);
-                store_a(m, m, aA);
+                store_a(m, m, aA, 0);
                 const f32x4 na = l_block(m, m, aL);  // N in accumulator layout (lane (x,g): N[4g+i][x])
 #pragma unroll
                 for (int i = 0; i < 4; ++i) L[o0 + 4 * g + i][o0 + x] = na[i];
@@ -808,7 +917,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     const f32x4 v = l_block(m, n, aL);
 #pragma unroll
                     for (int ii = 0; ii < 4; ++ii) L[16 * m + 4 * g + ii][16 * n + x] = v[ii];
-                    store_a(m, n, aA);
+                    store_a(m, n, aA, 0);
                 }
                 {
                     const int m = 3, n = 1 + (j & 1);
@@ -819,16 +928,17 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 #pragma unroll
                         for (int ii = 0; ii < 4; ++ii) L[16 * m + 4 * g + ii][16 * n + x] = v[ii];
                     } else {
-                        store_a(m, n, aA);
+                        store_a(m, n, aA, 1);
                     }
                 }
-                if (j < 2) {  // the all-zero upper A tiles inside used k-steps: (0,1) and (2,3)
+                if (!PAIR && j < 2) {  // the all-zero upper A tiles inside used k-steps: (0,1) and (2,3)
                     const int m = 2 * j, n = m + 1;
                     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    *reinterpret_cast<quad_t<T> *>(blk + BL::A_OFF + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) =
-                        make_quad<T>(z);
+                    *reinterpret_cast<quad_t<T> *>(bA + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) = make_quad<T>(z);
                 }
-                for (int f = j; f < 2 * KS; f += IWAVES - 4) qp_frag(f);  // first half of Q+
+                if constexpr (!PAIR) {  // first half of Q+ (pair mode: all of it in P3, KR is still being read)
+                    for (int f = j; f < 2 * KS; f += IWAVES - 4) qp_frag(f);
+                }
             }
         }
         lds_barrier();  // L and D complete; KR / KC fully read (Tp may overwrite the off-diagonal column operands)
@@ -841,6 +951,19 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             // a wait at the top of the next item would also wait for every P3/P4
             // store.
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
+            if constexpr (PAIR) {  // the A tiles held since P2, and the two zero tiles
+                auto put_a = [&](int m, int n, const f32x4 &a4) {
+                    *reinterpret_cast<quad_t<T> *>(bA + ((m * 2 + n / 2) * 64 + l) * 8 + 4 * (n % 2)) = make_quad<T>(a4);
+                };
+                if (w < 4) {
+                    put_a(w, w, apend0);
+                } else {
+                    const int j = w - 4;
+                    put_a(j == 0 ? 1 : (j == 3 ? 3 : 2), j == 2 ? 1 : 0, apend0);
+                    if (j >= 2) put_a(3, 1 + (j & 1), apend1);
+                    if (j < 2) put_a(2 * j, 2 * j + 1, f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+            }
             if (w < 4) {  // diagonal block of Tp
                 const float bc = sm.beta[16 * w + x];
 #pragma unroll
@@ -880,13 +1003,17 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     for (int e = 0; e < 4; ++e) z[e] = from_f<T>(0.f);
                     *reinterpret_cast<tok4 *>(&sm.y.t.Tp[16 * mb + r][16 * (mb + 1) + cq]) = z;
                 }
-                // (K gamma^C / Gamma)^T as the chain's A-operand fragments (rows
-                // channels, k tokens in kmap order), copied from LDS.
-                for (int f = w - 3; f < 2 * (DK / 16); f += IWAVES - 3) {
-                    const int R = f / 2, ks = f % 2;
-                    store8(blk + BL::KT_OFF + (f * 64 + l) * 8, load_frag_kmap<T>(&sm.KtT[16 * R + x][32 * ks], g));
+                if constexpr (PAIR) {  // K~^T stays in KtT; all of Q+ here
+                    for (int f = w - 3; f < 4 * KS; f += IWAVES - 3) qp_frag(f);
+                } else {
+                    // (K gamma^C / Gamma)^T as the chain's A-operand fragments (rows
+                    // channels, k tokens in kmap order), copied from LDS.
+                    for (int f = w - 3; f < 2 * (DK / 16); f += IWAVES - 3) {
+                        const int R = f / 2, ks = f % 2;
+                        store8(blk + BL::KT_OFF + (f * 64 + l) * 8, load_frag_kmap<T>(&sm.KtT[16 * R + x][32 * ks], g));
+                    }
+                    for (int f = 2 * KS + w - 3; f < 4 * KS; f += IWAVES - 3) qp_frag(f);  // second half of Q+
                 }
-                for (int f = 2 * KS + w - 3; f < 4 * KS; f += IWAVES - 3) qp_frag(f);  // second half of Q+
             }
             if constexpr (PRO) {
                 if (have2) prologue_regs(len2, sq2, lc2, slen2, h2);
@@ -912,7 +1039,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks <= m / 2; ++ks) acc = mma(tpf[m][ks], vt[ks], acc);
-                    *reinterpret_cast<quad_t<T> *>(blk + BL::U_OFF + ((ct * 4 + m) * 64 + l) * 4) = make_quad<T>(acc);
+                    *reinterpret_cast<quad_t<T> *>(bU + ((ct * 4 + m) * 64 + l) * 4) = make_quad<T>(acc);
                 }
             }
             for (int ct = w; ct < DK / 16; ct += IWAVES) {
@@ -924,14 +1051,133 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks <= tt / 2; ++ks) acc = mma(kp[ks], tpf[tt][ks], acc);
-                    *reinterpret_cast<quad_t<T> *>(blk + BL::W_OFF + ((tt * KS + ct / 2) * 64 + l) * 8 + 4 * (ct % 2)) =
-                        make_quad<T>(-acc);
+                    *reinterpret_cast<quad_t<T> *>(bW + ((tt * KS + ct / 2) * 64 + l) * 8 + 4 * (ct % 2)) = make_quad<T>(-acc);
                 }
             }
         }
-        lds_barrier();  // LDS is reused by the next item
+        lds_barrier();  // LDS is reused by the next item (pair mode: the block is complete)
+
+        // ---- pair mode: the chain step of this chunk, a column tile per wave --
+        // As in chain_wide_kernel, from the LDS block: V~ = U - W S, O^T = S^T (Q+)^T
+        // + V~^T A^T, S <- Diag(gamma^C) S + K~^T V~; o and checkpoints out; the
+        // final state after the pair's last chunk.  The next chunk's P1b writes
+        // these regions only after its first barrier, which every wave reaches
+        // after its share of this step.
+        if constexpr (PAIR) {
+            if (w < NCW) {
+                constexpr int FB = (int)sizeof(frag_t<T>), QB = (int)sizeof(quad_t<T>), EL = (int)sizeof(T);
+                const int ct0 = CT * w;
+                auto frag = [&](const T *base, int piece) {
+                    return *reinterpret_cast<const frag_t<T> *>(reinterpret_cast<const char *>(base) + piece * 64 * FB + l * FB);
+                };
+                frag_t<T> Sf[KS][CT];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            Sf[ks][cc][e] = from_f<T>(S[2 * ks][cc][e]);
+                            Sf[ks][cc][4 + e] = from_f<T>(S[2 * ks + 1][cc][e]);
+                        }
+                f32x4 V[4][CT];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int cc = 0; cc < CT; ++cc)
+                        V[m][cc] = quad_to_f<T>(*reinterpret_cast<const quad_t<T> *>(
+                            reinterpret_cast<const char *>(bU) + (((ct0 + cc) * 4 + m) * 64 + l) * QB));
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const frag_t<T> wf = frag(bW, m * KS + ks);
+#pragma unroll
+                        for (int cc = 0; cc < CT; ++cc) V[m][cc] = mma(wf, Sf[ks][cc], V[m][cc]);
+                    }
+                f32x4 O[CT][4];
+#pragma unroll
+                for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) O[cc][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const frag_t<T> qf = frag(bQ, m * KS + ks);
+#pragma unroll
+                        for (int cc = 0; cc < CT; ++cc) O[cc][m] = mma(Sf[ks][cc], qf, O[cc][m]);
+                    }
+                frag_t<T> Vf[2][CT];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            Vf[ks][cc][e] = from_f<T>(V[2 * ks][cc][e]);
+                            Vf[ks][cc][4 + e] = from_f<T>(V[2 * ks + 1][cc][e]);
+                        }
+#pragma unroll
+                for (int R = 0; R < NR; ++R) {
+                    const f32x4 gam = *reinterpret_cast<const f32x4 *>(&bG[16 * R + 4 * g]);
+#pragma unroll
+                    for (int cc = 0; cc < CT; ++cc) S[R][cc] *= gam;
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int R = 0; R < NR; ++R) {
+                        const frag_t<T> kf = load_frag_kmap<T>(&sm.KtT[16 * R + x][32 * ks], g);
+#pragma unroll
+                        for (int cc = 0; cc < CT; ++cc) S[R][cc] = mma(kf, Vf[ks][cc], S[R][cc]);
+                    }
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int ks = 0; ks <= m / 2; ++ks) {
+                        const frag_t<T> af = frag(bA, m * 2 + ks);
+#pragma unroll
+                        for (int cc = 0; cc < CT; ++cc) O[cc][m] = mma(Vf[ks][cc], af, O[cc][m]);
+                    }
+                // o through a descriptor whose record count ends at the chunk's last token
+                const int rowb = p.H * DV * EL;
+                const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)((T *)p.o + ((size_t)tok0 * p.H + h) * DV), 0, (len - 1) * rowb + DV * EL, 0x00020000);
+#pragma unroll
+                for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        buf_store<quad_t<T>>(ro, (16 * m + x) * rowb + (16 * (ct0 + cc) + 4 * g) * EL, make_quad<T>(O[cc][m]));
+                const size_t sb = ((size_t)sq * p.H + h) * DK * DV;
+                // prefix-state checkpoint after every ckpt_every-th chunk strictly inside the sequence
+                if (p.ckpt_every > 0 && (lc + 1) % p.ckpt_every == 0) {
+                    const int jk = (lc + 1) / p.ckpt_every - 1;
+                    if (jk < p.ckpt_slots && (lc + 1) * CHUNK < slen) {
+                        float *cp = p.ckpt + (((size_t)sq * p.ckpt_slots + jk) * p.H + h) * DK * DV;
+#pragma unroll
+                        for (int R = 0; R < NR; ++R)
+#pragma unroll
+                            for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    cp[(size_t)(16 * R + 4 * g + e) * DV + 16 * (ct0 + cc) + x] = S[R][cc][e];
+                    }
+                }
+                if (lc == nch - 1 && p.hT) {
+#pragma unroll
+                    for (int R = 0; R < NR; ++R)
+#pragma unroll
+                        for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                p.hT[sb + (size_t)(16 * R + 4 * g + e) * DV + 16 * (ct0 + cc) + x] = S[R][cc][e];
+                }
+            }
+        }
         i = i2; c = c2; h = h2; tok0 = tok2; len = len2;
         sq = sq2; lc = lc2; slen = slen2;
+        pst = pst2; nch = nch2;
         have = have2;
     }
 }
@@ -1489,6 +1735,32 @@ static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
         hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(table::THREADS), 0, st, p.cu, p.N, p.T, p.n_chunks_cap,
                            p.chunk_off, p.order, p.span);
     const bool pro = p.f.conv_w > 0;  // the prologue runs inside the intra-chunk stage
+    const long npairs = (long)p.N * p.H;
+    // Many pairs (bf16, d_k = 128, no prologue): the chain runs inside the
+    // intra-chunk kernel (pair mode), one workgroup per compute unit.
+    constexpr bool PAIR_OK = sizeof(T) == 2 && DK == 128;
+    if (PAIR_OK && !pro && npairs >= WIDE_CHAIN_PAIRS && p.n_chunks_cap > 0) {
+        const size_t smem = sizeof(IntraSmem<T, DK, DV>);
+        static const hipError_t attr[2] = {
+            hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, true, false, PAIR_OK>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem),
+            hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, false, false, PAIR_OK>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem)};
+        for (hipError_t e : attr)
+            if (e != hipSuccess) return e;
+        const unsigned grid = (unsigned)(npairs < intra_grid() ? npairs : intra_grid());
+        if (p.A_log)
+            hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, true, false, PAIR_OK>), dim3(grid), dim3(64 * IWAVES), smem, st, p);
+        else
+            hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, false, false, PAIR_OK>), dim3(grid), dim3(64 * IWAVES), smem, st, p);
+        const long rows = (long)(p.varlen ? p.T : (long)p.N * p.T) * p.H;
+        if (p.f.gate && rows > 0) {
+            constexpr int RPB = 4 * (64 / (DV / (16 / (int)sizeof(T))));  // rows per 256-thread workgroup
+            hipLaunchKernelGGL((gate_norm_kernel<T, DV>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
+                               (T *)p.o, (const T *)p.f.gate, p.f.o_weight, p.H, rows, p.f.o_eps);
+        }
+        return hipGetLastError();
+    }
     if (p.n_chunks_cap > 0) {
         const size_t smem = sizeof(IntraSmem<T, DK, DV>);
         static_assert(sizeof(IntraSmem<T, DK, DV>) <= 160 * 1024, "intra-chunk LDS exceeds 160 KiB");
@@ -1514,7 +1786,6 @@ static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
             else hipLaunchKernelGGL((intra_chunk_kernel<T, DK, DV, false, false>), gd, bd, smem, st, p);
         }
     }
-    const long npairs = (long)p.N * p.H;
     if (npairs >= WIDE_CHAIN_PAIRS) {
         hipLaunchKernelGGL((chain_wide_kernel<T, DK, DV>), dim3((unsigned)npairs), dim3(256), 0, st, p);
     } else {
