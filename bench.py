@@ -463,8 +463,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-PREFILL_KERNELS = ("kda_chunk_fwd (intra_chunk_kernel + chain_kernel, or chain_wide_kernel from 128 "
-                   "(sequence, head) pairs; chunk_table_kernel for packed input)")
+PREFILL_KERNELS = ("kda_chunk_fwd (from 128 (sequence, head) pairs at bf16, d_k = 128: intra_chunk_kernel in pair "
+                   "mode, the chain inside it; below: intra_chunk_kernel + chain_kernel; chunk_table_kernel for "
+                   "packed input)")
 HEADLINE = "varlen_64"
 
 

@@ -137,8 +137,11 @@ kda_status_t plan_chunk(const kda_chunk_fwd_args_t *a, ChunkPlan *pl)
     pl->n_chunks_cap = (int)cap;
     pl->table = kda::table_bytes(pl->varlen, pl->N);
     pl->block = block;
-    pl->blocks = (size_t)a->H * (size_t)cap * block;
-    pl->total = pl->table + pl->blocks;  // the layer prologue needs no workspace (it runs in registers)
+    // pair mode keeps every chunk block in LDS; the layer prologue runs in registers
+    const int pro = a->fusion && a->fusion->conv_width > 0;
+    const bool pairs = kda::pair_mode(a->dtype == KDA_BF16, a->Dk, (long)pl->N * a->H, pro);
+    pl->blocks = pairs ? 0 : (size_t)a->H * (size_t)cap * block;
+    pl->total = pl->table + pl->blocks;
     return KDA_SUCCESS;
 }
 

@@ -41,6 +41,15 @@ struct PrefillParams {
     FusionParams f;
 };
 
+// With this many (sequence, head) pairs or more the chain stage runs per pair:
+// inside the intra-chunk kernel (pair mode, no chunk blocks in the workspace)
+// for bf16 with d_k = 128 and no layer prologue, else on the wide chain kernel.
+constexpr long MANY_PAIRS = 128;
+inline bool pair_mode(int bf16, int Dk, long npairs, int prologue)
+{
+    return bf16 && Dk == 128 && !prologue && npairs >= MANY_PAIRS;
+}
+
 // Bytes of one (head, chunk) workspace block; 0 if the combination is unsupported.
 size_t block_bytes(int bf16, int Dk, int Dv);
 

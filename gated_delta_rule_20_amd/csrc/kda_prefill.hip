@@ -1707,11 +1707,12 @@ __global__ __launch_bounds__(256) void empty_conv_state_kernel(const PrefillPara
         ((T *)p.f.conv_state_out)[base + e] = p.f.conv_state ? ((const T *)p.f.conv_state)[base + e] : from_f<T>(0.f);
 }
 
-// With this many (sequence, head) pairs or more the chain runs on the wide
-// kernel (one compute unit per pair, about 2.7 times less work per chunk than
-// the slice kernel's eight, each chunk about 3 times slower); below it the
-// slice kernel's shorter time per chunk wins.
-constexpr long WIDE_CHAIN_PAIRS = 128;
+// From MANY_PAIRS (sequence, head) pairs on, the chain runs per pair: in pair
+// mode inside the intra-chunk kernel, else on the wide kernel (one compute unit
+// per pair, about 2.7 times less work per chunk than the slice kernel's eight,
+// each chunk about 3 times slower); below it the slice kernel's shorter time
+// per chunk wins.
+constexpr long WIDE_CHAIN_PAIRS = MANY_PAIRS;
 
 // -----------------------------------------------------------------------------
 // Persistent grid of the intra-chunk stage: one workgroup per compute unit
@@ -1739,7 +1740,7 @@ static hipError_t launch_t(const PrefillParams &p, hipStream_t st)
     // Many pairs (bf16, d_k = 128, no prologue): the chain runs inside the
     // intra-chunk kernel (pair mode), one workgroup per compute unit.
     constexpr bool PAIR_OK = sizeof(T) == 2 && DK == 128;
-    if (PAIR_OK && !pro && npairs >= WIDE_CHAIN_PAIRS && p.n_chunks_cap > 0) {
+    if (pair_mode(sizeof(T) == 2, DK, npairs, pro) && p.n_chunks_cap > 0) {
         const size_t smem = sizeof(IntraSmem<T, DK, DV>);
         static const hipError_t attr[2] = {
             hipFuncSetAttribute((const void *)intra_chunk_kernel<T, DK, DV, true, false, PAIR_OK>,

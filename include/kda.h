@@ -151,8 +151,12 @@ typedef struct {
  *                   token, or NULL if not wanted.
  * Dk, Dv in {64, 128}.  T may be 0 (then final_state = initial_state).
  * The workspace (device memory, >= kda_chunk_fwd_workspace_size bytes,
- * 256-byte aligned) holds per-chunk intermediates; its contents on entry are
- * ignored and on exit are unspecified.
+ * 256-byte aligned) holds the packed-sequence chunk table and per-chunk
+ * intermediates; its contents on entry are ignored and on exit are
+ * unspecified.  With bf16 inputs, Dk = 128, no layer prologue and 128 or more
+ * (sequence, head) pairs the per-chunk intermediates stay on chip and the
+ * workspace holds the chunk table only (none for a batch of equal-length
+ * sequences).
  *
  * State checkpoints ("Kimi K3 Technical Report", §5.4.1: the KDA state is
  * persisted at hash-block-aligned prefix positions so that a later request
@@ -205,8 +209,9 @@ KDA_API kda_status_t kda_chunk_fwd(const kda_chunk_fwd_args_t *args, void *strea
  * process ends.  args->workspace must be NULL and args->workspace_bytes 0.
  * Shapes whose kda_chunk_fwd_workspace_size exceeds the array are rejected
  * with KDA_ERROR_WORKSPACE before anything is enqueued (at bf16 and
- * Dk = Dv = 128 the array holds 897 chunk blocks of
- * 64 tokens x 1 head, e.g. B = 1, T = 7168 tokens at H = 8).  The array used
+ * Dk = Dv = 128 with fewer than 128 (sequence, head) pairs the array holds
+ * 897 chunk blocks of 64 tokens x 1 head, e.g. B = 1, T = 7168 tokens at
+ * H = 8; with 128 pairs or more it needs only the chunk table).  The array used
  * is the copy on the device that is current when the call is made, which must
  * be the stream's device.  Every call on one device uses the same array, so
  * calls that overlap on a device (on different streams, or from different

@@ -345,7 +345,7 @@ def test_noalloc_limit_matches_header():
     (dict(workspace_bytes=4096), 1, "takes no workspace"),
     (dict(T=8192, H=32), 3, "holds at most"),
     (dict(T=7232, H=8), 3, "holds at most"),               # 113 chunks x 8 heads: one chunk over
-    (dict(T=7000, H=8, cu_seqlens=0x20000, N=64), 3, "holds at most"),
+    (dict(T=7000, H=8, cu_seqlens=0x20000, N=8), 3, "holds at most"),  # 64 pairs: chunk blocks in the workspace
     (dict(Dk=96), 2, "head dims"),
 ])
 def test_chunk_fwd_noalloc_rejects_before_device_work(lib, over, status, msg):
@@ -365,3 +365,24 @@ def test_noalloc_array_holds_the_documented_largest_call(lib):
     assert st == 0 and n <= kda.NOALLOC_WORKSPACE_BYTES
     st, n = _ws(lib, _args(T=7169, H=8))
     assert st == 0 and n > kda.NOALLOC_WORKSPACE_BYTES
+
+
+def test_pair_mode_workspace_is_the_table(lib):
+    """From 128 (sequence, head) pairs on (bf16, Dk = 128, no prologue) the chunk
+    blocks stay on chip: the workspace is the chunk table (packed input) or
+    nothing (a batch); with the prologue, float32, Dk = 64 or fewer pairs the
+    blocks are there."""
+    st, n = _ws(lib, _args(T=1000, cu_seqlens=0x20000, N=64, H=2))  # 128 pairs
+    assert st == 0 and n == 1280                                        # (4 N + 1) int32, to 256 B
+    st, n = _ws(lib, _args(B=128, T=100, H=1))
+    assert st == 0 and n == 0
+    block = 74752
+    st, n = _ws(lib, _args(B=127, T=100, H=1))                          # 127 pairs
+    assert st == 0 and n == 127 * 2 * block
+    st, n = _ws(lib, _args(B=128, T=100, H=1, Dk=64))
+    assert st == 0 and n > 0
+    a = _args(B=128, T=100, H=1)
+    f = _fusion()
+    a.fusion = ctypes.pointer(f)
+    out = ctypes.c_size_t(0)
+    assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(out)) == 0 and out.value == 128 * 2 * block
