@@ -1070,85 +1070,81 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 auto frag = [&](const T *base, int piece) {
                     return *reinterpret_cast<const frag_t<T> *>(reinterpret_cast<const char *>(base) + piece * 64 * FB + l * FB);
                 };
-                frag_t<T> Sf[KS][CT];
+                static_assert(CT == 1 && KS == 4, "pair mode chain step: one column tile, d_k = 128");
+                frag_t<T> Sf[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                    for (int cc = 0; cc < CT; ++cc)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            Sf[ks][cc][e] = from_f<T>(S[2 * ks][cc][e]);
-                            Sf[ks][cc][4 + e] = from_f<T>(S[2 * ks + 1][cc][e]);
-                        }
-                f32x4 V[4][CT];
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-#pragma unroll
-                    for (int cc = 0; cc < CT; ++cc)
-                        V[m][cc] = quad_to_f<T>(*reinterpret_cast<const quad_t<T> *>(
-                            reinterpret_cast<const char *>(bU) + (((ct0 + cc) * 4 + m) * 64 + l) * QB));
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const frag_t<T> wf = frag(bW, m * KS + ks);
-#pragma unroll
-                        for (int cc = 0; cc < CT; ++cc) V[m][cc] = mma(wf, Sf[ks][cc], V[m][cc]);
+                    for (int e = 0; e < 4; ++e) {
+                        Sf[ks][e] = from_f<T>(S[2 * ks][0][e]);
+                        Sf[ks][4 + e] = from_f<T>(S[2 * ks + 1][0][e]);
                     }
-                f32x4 O[CT][4];
+                f32x4 V[4], O[4];
 #pragma unroll
-                for (int cc = 0; cc < CT; ++cc)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) O[cc][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const frag_t<T> qf = frag(bQ, m * KS + ks);
-#pragma unroll
-                        for (int cc = 0; cc < CT; ++cc) O[cc][m] = mma(Sf[ks][cc], qf, O[cc][m]);
-                    }
-                frag_t<T> Vf[2][CT];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int cc = 0; cc < CT; ++cc)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            Vf[ks][cc][e] = from_f<T>(V[2 * ks][cc][e]);
-                            Vf[ks][cc][4 + e] = from_f<T>(V[2 * ks + 1][cc][e]);
-                        }
-#pragma unroll
-                for (int R = 0; R < NR; ++R) {
-                    const f32x4 gam = *reinterpret_cast<const f32x4 *>(&bG[16 * R + 4 * g]);
-#pragma unroll
-                    for (int cc = 0; cc < CT; ++cc) S[R][cc] *= gam;
+                for (int m = 0; m < 4; ++m) {
+                    V[m] = quad_to_f<T>(*reinterpret_cast<const quad_t<T> *>(
+                        reinterpret_cast<const char *>(bU) + ((ct0 * 4 + m) * 64 + l) * QB));
+                    O[m] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int R = 0; R < NR; ++R) {
-                        const frag_t<T> kf = load_frag_kmap<T>(&sm.KtT[16 * R + x][32 * ks], g);
-#pragma unroll
-                        for (int cc = 0; cc < CT; ++cc) S[R][cc] = mma(kf, Vf[ks][cc], S[R][cc]);
+                frag_t<T> Vf[2];
+                // The step's 54 products, in order: V~ = U - W S (W pieces 0-15, piece
+                // m KS + ks), O^T = S^T (Q+)^T (Q+ pieces 0-15), S <- Diag(gamma^C) S +
+                // K~^T V~ (K~^T row tile q / 2, k-step q % 2, from KtT), O^T += V~^T A^T
+                // (A pieces 0, 2, 4, 5, 6, 7: A is lower triangular, so token tiles 0 and 1
+                // have one k-step).  Operands are read from LDS four at a time, one group
+                // ahead of the products, so that LDS latency overlaps MFMA work.
+                constexpr int NP = 54, GP = 4;
+                auto fetch = [&](int i) -> frag_t<T> {
+                    if (i < 16) return frag(bW, i);
+                    if (i < 32) return frag(bQ, i - 16);
+                    if (i < 48) return load_frag_kmap<T>(&sm.KtT[16 * ((i - 32) / 2) + x][32 * ((i - 32) % 2)], g);
+                    const int j = i - 48;
+                    return frag(bA, j < 2 ? 2 * j : j + 2);
+                };
+                auto apply = [&](int i, const frag_t<T> &f) {
+                    if (i < 16) {
+                        V[i / KS] = mma(f, Sf[i % KS], V[i / KS]);
+                    } else if (i < 32) {
+                        O[(i - 16) / KS] = mma(Sf[(i - 16) % KS], f, O[(i - 16) / KS]);
+                    } else if (i < 48) {
+                        S[(i - 32) / 2][0] = mma(f, Vf[(i - 32) % 2], S[(i - 32) / 2][0]);
+                    } else {
+                        const int j = i - 48, m = j < 2 ? j : 2 + (j - 2) / 2;
+                        O[m] = mma(Vf[j < 2 ? 0 : (j - 2) % 2], f, O[m]);
                     }
+                };
+                frag_t<T> cur[GP], nxt[GP];
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
+                for (int q = 0; q < GP; ++q) cur[q] = fetch(q);
 #pragma unroll
-                    for (int ks = 0; ks <= m / 2; ++ks) {
-                        const frag_t<T> af = frag(bA, m * 2 + ks);
+                for (int i0 = 0; i0 < NP; i0 += GP) {
 #pragma unroll
-                        for (int cc = 0; cc < CT; ++cc) O[cc][m] = mma(Vf[ks][cc], af, O[cc][m]);
-                    }
+                    for (int q = 0; q < GP; ++q)
+                        if (i0 + GP + q < NP) nxt[q] = fetch(i0 + GP + q);
+                    // Diag(gamma^C) S, one row tile per group while the fragments above
+                    // (which hold S) feed the first products
+                    if (i0 < 4 * NR) S[i0 / 4][0] *= *reinterpret_cast<const f32x4 *>(&bG[16 * (i0 / 4) + 4 * g]);
+                    if (i0 == 32)  // V~ complete: its B fragments
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                Vf[ks][e] = from_f<T>(V[2 * ks][e]);
+                                Vf[ks][4 + e] = from_f<T>(V[2 * ks + 1][e]);
+                            }
+#pragma unroll
+                    for (int q = 0; q < GP; ++q)
+                        if (i0 + q < NP) apply(i0 + q, cur[q]);
+#pragma unroll
+                    for (int q = 0; q < GP; ++q) cur[q] = nxt[q];
+                }
                 // o through a descriptor whose record count ends at the chunk's last token
                 const int rowb = p.H * DV * EL;
                 const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
                     (void *)((T *)p.o + ((size_t)tok0 * p.H + h) * DV), 0, (len - 1) * rowb + DV * EL, 0x00020000);
 #pragma unroll
-                for (int cc = 0; cc < CT; ++cc)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        buf_store<quad_t<T>>(ro, (16 * m + x) * rowb + (16 * (ct0 + cc) + 4 * g) * EL, make_quad<T>(O[cc][m]));
+                for (int m = 0; m < 4; ++m)
+                    buf_store<quad_t<T>>(ro, (16 * m + x) * rowb + (16 * ct0 + 4 * g) * EL, make_quad<T>(O[m]));
                 const size_t sb = ((size_t)sq * p.H + h) * DK * DV;
                 // prefix-state checkpoint after every ckpt_every-th chunk strictly inside the sequence
                 if (p.ckpt_every > 0 && (lc + 1) % p.ckpt_every == 0) {
