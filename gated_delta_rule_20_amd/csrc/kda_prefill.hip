@@ -144,9 +144,29 @@ template <typename T, int N> struct Vec { typedef T type __attribute__((ext_vect
 
 constexpr float LOG2E = 1.4426950408889634f;
 
+// LDS layouts.  The pitches and the XOR swizzles below keep every access of the
+// kernel free of LDS bank conflicts on gfx950, whose LDS serves a 16-byte read
+// for lanes {0-3, 20-23}, {4-7, 16-19}, {8-11, 28-31}, {12-15, 24-27} (and the
+// same +32) on 32 four-byte banks, an 8-byte read for 32 lanes on 64 banks, and
+// each address of a two-address 8-byte read for 16 consecutive lanes on 32 banks
+// (measured with the bank-conflict counter).  Swizzles permute 8-element blocks
+// within a row, so 16-byte fragments stay contiguous.
+//
+// Token-major operand rows (KR, QR, KC) hold each 32-channel k-step in the
+// fragment order of the chain's products (channels 4j..4j+3 and 16+4j..16+4j+3
+// at 8j..8j+7): the Q+ fragments are then plain 16-byte reads, and the Gram
+// products, which read the same positions from the rows they pair, are
+// unchanged (kpos gives the position of a channel).
+// KpT, VT (row = channel): 8-token block b of row r sits at b ^ swz_kv(r).
+__device__ __forceinline__ int swz_kv(int r) { return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2); }
+// Tp (row = token): 8-column block b of row r sits at b ^ swz_tp(r).
+__device__ __forceinline__ int swz_tp(int r) { return (r >> 2) & 1; }
+
 template <typename T, int DK, int DV> struct IntraSmem {
-    static constexpr int PR = DK + 8;     // padded row of token-major arrays
-    static constexpr int PT = CHUNK + 8;  // padded row of channel-major arrays
+    static constexpr int PR = DK + 16;    // row of the token-major operand arrays
+    static constexpr int PT = CHUNK + 8;  // row of Tp
+    static constexpr int PV = CHUNK;      // row of KpT and VT (swizzled)
+    static constexpr int PK = CHUNK + 4;  // row of KtT: its 16-byte writes and two-address 8-byte reads stay conflict-free
     static constexpr int LP = CHUNK + 4;  // fp32 row pitch of L and its inverse
     // Column-operand rows: [0,64) exp(B_n - lam) for tile n (diagonal pairs);
     // [64,112) exp(B_{n+1} - lam) for tiles 0..2 (pairs (n+1, n)); [112,128)
@@ -166,9 +186,9 @@ template <typename T, int DK, int DV> struct IntraSmem {
             T Tp[CHUNK][PT];    // (I + L)^-1 Diag(beta) (P3 -> P4)
         } t;
     } y;
-    T KpT[DK][PT];         // (k * exp(lam))^T, A operand of W^T
-    T KtT[DK][PT];         // (k * exp(lam_C - lam))^T, copied out as the chain's K~^T fragments (P1 -> P3)
-    T VT[DV][PT];          // v^T, B operand of U
+    T KpT[DK][PV];         // (k * exp(lam))^T, A operand of W^T
+    T KtT[DK][PK];         // (k * exp(lam_C - lam))^T, copied out as the chain's K~^T fragments (P1 -> P3)
+    T VT[DV][PV];          // v^T, B operand of U
     float tot[8][DK];      // half-tile (8-token segment) totals (log2 units)
     float eB[4][DK];       // exp(B_m) per tile and channel (P1 -> P3)
     float beta[CHUNK];
@@ -713,17 +733,24 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         lds_barrier();
         {
             float eBm[CPT], eCB[CPT], eT[CPT], eX1[CPT], eX2[CPT], gC[CPT];
+            // a lane's CPT channels of each half-tile total in one read (single
+            // 4-byte reads at an 8-byte lane stride would meet in the LDS banks)
+            typedef typename Vec<float, CPT>::type fc;
+            fc sgv[8];
+#pragma unroll
+            for (int q2 = 0; q2 < 8; ++q2) sgv[q2] = *reinterpret_cast<const fc *>(&sm.tot[q2][ch0]);
+            const fc hofv = *reinterpret_cast<const fc *>(&sm.tot[2 * m0][ch0]);
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) {
                 float sg[8];
 #pragma unroll
-                for (int q2 = 0; q2 < 8; ++q2) sg[q2] = sm.tot[q2][ch0 + cc];
+                for (int q2 = 0; q2 < 8; ++q2) sg[q2] = sgv[q2][cc];
                 const float t0 = sg[0] + sg[1], t1 = sg[2] + sg[3], t2 = sg[4] + sg[5], t3 = sg[6] + sg[7];
                 const float Bm = (m0 > 0 ? t0 : 0.f) + (m0 > 1 ? t1 : 0.f) + (m0 > 2 ? t2 : 0.f);
                 const float C2 = t0 + t1 + t2 + t3;
                 // first half of the tile, for the second half (read from LDS: a
                 // register array indexed by the wave's tile would go to scratch)
-                const float hoff = hf ? sm.tot[2 * m0][ch0 + cc] : 0.f;
+                const float hoff = hf ? hofv[cc] : 0.f;
 #pragma unroll
                 for (int r = 0; r < HT; ++r) lam2[r][cc] += hoff;
                 eBm[cc] = __builtin_amdgcn_exp2f(Bm);              // exp(B_m)            <= 1
@@ -759,15 +786,16 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     kpv[cc][r0] = from_f<T>(kr * eBm[cc]);
                     ktv[cc][r0] = from_f<T>(kcs * eCB[cc]);
                 }
-                *reinterpret_cast<ku *>(&sm.ops.KR[tok][ch0]) = kr_;
-                *reinterpret_cast<ku *>(&sm.ops.QR[tok][ch0]) = qr_;
-                *reinterpret_cast<ku *>(&sm.y.KC[tok][ch0]) = kc_;
-                if (m0 < 3) *reinterpret_cast<ku *>(&sm.y.KC[64 + tok][ch0]) = ke_;
+                const int cp = kpos(ch0);  // CPT <= 2 channels stay adjacent
+                *reinterpret_cast<ku *>(&sm.ops.KR[tok][cp]) = kr_;
+                *reinterpret_cast<ku *>(&sm.ops.QR[tok][cp]) = qr_;
+                *reinterpret_cast<ku *>(&sm.y.KC[tok][cp]) = kc_;
+                if (m0 < 3) *reinterpret_cast<ku *>(&sm.y.KC[64 + tok][cp]) = ke_;
                 if (m0 == 0) {
-                    *reinterpret_cast<ku *>(&sm.y.KC[112 + r][ch0]) = kx1_;
-                    *reinterpret_cast<ku *>(&sm.y.KC[128 + r][ch0]) = kx2_;
+                    *reinterpret_cast<ku *>(&sm.y.KC[112 + r][cp]) = kx1_;
+                    *reinterpret_cast<ku *>(&sm.y.KC[128 + r][cp]) = kx2_;
                 }
-                if (m0 == 1) *reinterpret_cast<ku *>(&sm.y.KC[144 + r][ch0]) = kx1_;
+                if (m0 == 1) *reinterpret_cast<ku *>(&sm.y.KC[144 + r][cp]) = kx1_;
                 raw.g[r0] = buf_load<ku>(rsg, offk + r0 * rowk);
                 raw.k[r0] = buf_load<ku>(rsk, offk + r0 * rowk);
                 raw.q[r0] = buf_load<ku>(rsq, offk + r0 * rowk);
@@ -775,7 +803,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) {
                 const int ch = ch0 + cc;
-                *reinterpret_cast<tok8 *>(&sm.KpT[ch][tb]) = kpv[cc];
+                *reinterpret_cast<tok8 *>(&sm.KpT[ch][tb ^ (8 * swz_kv(ch))]) = kpv[cc];
                 *reinterpret_cast<tok8 *>(&sm.KtT[ch][tb]) = ktv[cc];
             }
             if (w == 0) {  // gamma^C, stored after the last use of the raw registers
@@ -787,7 +815,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 tok8 col;
 #pragma unroll
                 for (int r = 0; r < HT; ++r) col[r] = raw.v[r][cv];
-                *reinterpret_cast<tok8 *>(&sm.VT[CPV * l + cv][tb]) = col;
+                *reinterpret_cast<tok8 *>(&sm.VT[CPV * l + cv][tb ^ (8 * swz_kv(CPV * l + cv))]) = col;
             }
 #pragma unroll
             for (int r = 0; r < HT; ++r) raw.v[r] = buf_load<typename R::vu>(rsv, offv + r * rowv);
@@ -799,7 +827,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         // is token tile f / KS, k-step f % KS.
         auto qp_frag = [&](int f) {
             const int m = f / KS, ks = f % KS;
-            const frag_t<T> qr = load_frag_kmap<T>(&sm.ops.QR[16 * m + x][32 * ks], g);
+            const frag_t<T> qr = load_frag_lin<T>(&sm.ops.QR[16 * m + x][32 * ks], g);
             const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 4 * g]);
             const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&sm.eB[m][32 * ks + 16 + 4 * g]);
             frag_t<T> qp;
@@ -967,7 +995,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             if (w < 4) {  // diagonal block of Tp
                 const float bc = sm.beta[16 * w + x];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sm.y.t.Tp[16 * w + 4 * g + i][16 * w + x] = from_f<T>(dmv[i] * bc);
+                for (int i = 0; i < 4; ++i) sm.y.t.Tp[16 * w + 4 * g + i][(16 * w + x) ^ (8 * swz_tp(4 * g + i))] = from_f<T>(dmv[i] * bc);
             }
             if (w < 3) {
                 const int n = w;
@@ -991,7 +1019,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     for (int i = 0; i < 4; ++i) tm = __builtin_amdgcn_mfma_f32_16x16x4f32(dm[i], acc[i], tm, 0, 0, 0);
                     Tr[d] = -tm;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sm.y.t.Tp[16 * m + 4 * g + i][16 * n + x] = from_f<T>(Tr[d][i] * bc);
+                    for (int i = 0; i < 4; ++i) sm.y.t.Tp[16 * m + 4 * g + i][(16 * n + x) ^ (8 * swz_tp(4 * g + i))] = from_f<T>(Tr[d][i] * bc);
                 }
             } else {
                 // Of the zero upper blocks of Tp, P4 reads only (0,1) and (2,3)
@@ -1001,7 +1029,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     tok4 z;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) z[e] = from_f<T>(0.f);
-                    *reinterpret_cast<tok4 *>(&sm.y.t.Tp[16 * mb + r][16 * (mb + 1) + cq]) = z;
+                    *reinterpret_cast<tok4 *>(&sm.y.t.Tp[16 * mb + r][(16 * (mb + 1) + cq) ^ (8 * swz_tp(r))]) = z;
                 }
                 if constexpr (PAIR) {  // K~^T stays in KtT; all of Q+ here
                     for (int f = w - 3; f < 4 * KS; f += IWAVES - 3) qp_frag(f);
@@ -1029,11 +1057,11 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int ks = 0; ks <= m / 2; ++ks) tpf[m][ks] = load_frag_lin<T>(&sm.y.t.Tp[16 * m + x][32 * ks], g);
+                for (int ks = 0; ks <= m / 2; ++ks) tpf[m][ks] = load8(&sm.y.t.Tp[16 * m + x][32 * ks + 8 * (g ^ swz_tp(x))]);
             for (int ct = w; ct < DV / 16; ct += IWAVES) {
                 frag_t<T> vt[2];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) vt[ks] = load_frag_lin<T>(&sm.VT[16 * ct + x][32 * ks], g);
+                for (int ks = 0; ks < 2; ++ks) vt[ks] = load8(&sm.VT[16 * ct + x][8 * ((4 * ks + g) ^ swz_kv(16 * ct + x))]);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1045,7 +1073,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
             for (int ct = w; ct < DK / 16; ct += IWAVES) {
                 frag_t<T> kp[2];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) kp[ks] = load_frag_lin<T>(&sm.KpT[16 * ct + x][32 * ks], g);
+                for (int ks = 0; ks < 2; ++ks) kp[ks] = load8(&sm.KpT[16 * ct + x][8 * ((4 * ks + g) ^ swz_kv(16 * ct + x))]);
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
