@@ -161,6 +161,9 @@ constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ int swz_kv(int r) { return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2); }
 // Tp (row = token): 8-column block b of row r sits at b ^ swz_tp(r).
 __device__ __forceinline__ int swz_tp(int r) { return (r >> 2) & 1; }
+// L and the D blocks inside it (fp32): column c of row r sits at c ^ swz_l(r),
+// which moves 4-column groups within 8-column groups.
+__device__ __forceinline__ int swz_l(int r) { return 4 * ((r >> 2) & 1); }
 
 template <typename T, int DK, int DV> struct IntraSmem {
     static constexpr int PR = DK + 16;    // row of the token-major operand arrays
@@ -913,9 +916,9 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 store_a(m, m, aA, 0);
                 const f32x4 na = l_block(m, m, aL);  // N in accumulator layout (lane (x,g): N[4g+i][x])
 #pragma unroll
-                for (int i = 0; i < 4; ++i) L[o0 + 4 * g + i][o0 + x] = na[i];
+                for (int i = 0; i < 4; ++i) L[o0 + 4 * g + i][(o0 + x) ^ swz_l(4 * g + i)] = na[i];
                 // N in row layout (lane (x,g): N[x][4g+i]), read back transposed by this wave
-                const f32x4 nr = *reinterpret_cast<const f32x4 *>(&L[o0 + x][o0 + 4 * g]);
+                const f32x4 nr = *reinterpret_cast<const f32x4 *>(&L[o0 + x][(o0 + 4 * g) ^ swz_l(x)]);
                 auto mm = [](const f32x4 &a, const f32x4 &b) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -936,7 +939,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 dmv = a3 + mm(a3t, n8);
                 float *Dm = dblk(sm, w);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Dm[(4 * g + i) * LP + x] = dmv[i];
+                for (int i = 0; i < 4; ++i) Dm[(4 * g + i) * LP + (x ^ swz_l(4 * g + i))] = dmv[i];
             } else {
                 const int j = w - 4;
                 {  // (1,0), (2,0), (2,1), (3,0)
@@ -944,7 +947,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     pair_products(m, n, true, true, aL, aA);
                     const f32x4 v = l_block(m, n, aL);
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) L[16 * m + 4 * g + ii][16 * n + x] = v[ii];
+                    for (int ii = 0; ii < 4; ++ii) L[16 * m + 4 * g + ii][(16 * n + x) ^ swz_l(4 * g + ii)] = v[ii];
                     store_a(m, n, aA, 0);
                 }
                 {
@@ -954,7 +957,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     if (doL) {
                         const f32x4 v = l_block(m, n, aL);
 #pragma unroll
-                        for (int ii = 0; ii < 4; ++ii) L[16 * m + 4 * g + ii][16 * n + x] = v[ii];
+                        for (int ii = 0; ii < 4; ++ii) L[16 * m + 4 * g + ii][(16 * n + x) ^ swz_l(4 * g + ii)] = v[ii];
                     } else {
                         store_a(m, n, aA, 1);
                     }
@@ -1009,11 +1012,11 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int qd = 0; qd < d; ++qd) {
-                        const f32x4 a = *reinterpret_cast<const f32x4 *>(&L[16 * m + x][16 * (n + qd) + 4 * g]);
+                        const f32x4 a = *reinterpret_cast<const f32x4 *>(&L[16 * m + x][(16 * (n + qd) + 4 * g) ^ swz_l(x)]);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], Tr[qd][i], acc, 0, 0, 0);
                     }
-                    const f32x4 dm = *reinterpret_cast<const f32x4 *>(dblk(sm, m) + x * LP + 4 * g);
+                    const f32x4 dm = *reinterpret_cast<const f32x4 *>(dblk(sm, m) + x * LP + ((4 * g) ^ swz_l(x)));
                     f32x4 tm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) tm = __builtin_amdgcn_mfma_f32_16x16x4f32(dm[i], acc[i], tm, 0, 0, 0);
@@ -1311,12 +1314,14 @@ __global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
     using BL = Block<T, DK, DV>;
     using LD = ChainLoad<T, DK, DV>;
     constexpr int KS = DK / 32, RT = DK / 64, NS = DV / 16;
-    constexpr int PS = DK + 8, PV = CHUNK + 8;
     // S^T and V~^T slices, [column][k], with k stored in kmap order inside each
     // block of 32 (position 8g + e holds k = kmap(g, e)), so an operand fragment
     // is one contiguous 16-byte read and an accumulator quad one 8-byte write.
-    __shared__ __align__(16) T sST[16][PS];
-    __shared__ __align__(16) T sVT[16][PV];
+    // Unpadded rows; 8-element block b of row x sits at b ^ (x & 7), which keeps
+    // the fragment reads free of LDS bank conflicts (the quad writes, 16 lanes
+    // at one 8-byte offset of a 16-byte block, cannot avoid a two-way conflict).
+    __shared__ __align__(16) T sST[16][DK];
+    __shared__ __align__(16) T sVT[16][CHUNK];
 
     const int npairs = p.N * p.H;
     const int bid = blockIdx.x, xcd = bid & 7, jj = bid >> 3;
@@ -1339,7 +1344,7 @@ __global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
     }
     const int t = threadIdx.x, wr = __builtin_amdgcn_readfirstlane(t >> 6), w = wr & 3;
     const int l = t & 63, g = l >> 4, x = l & 15;
-    const int col = 16 * sl + x;
+    const int col = 16 * sl + x, xsw = 8 * (x & 7);  // the row's block swizzle, in elements
     const size_t sbase = ((size_t)s * p.H + h) * DK * DV;
     const char *blk0 = p.blocks + ((size_t)h * p.n_chunks_cap + chunk0) * BL::BYTES;
     auto blk = [&](int lc) { return blk0 + (size_t)min(lc, nch - 1) * BL::BYTES; };  // last block again at the end
@@ -1355,25 +1360,25 @@ __global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
                 const int row = 16 * (w * RT + rt) + 4 * g + i;
                 S[rt][i] = p.h0 ? p.h0[sbase + (size_t)row * DV + col] : 0.f;
             }
-            *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
+            *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g) ^ xsw]) = make_quad<T>(S[rt]);
         }
         auto step = [&](const ChainRec<T, DK> &f, int lc, ChainRec<T, DK> &nx, int nlc) {
             const char *nb = blk(nlc);
             lds_barrier();  // S^T of this chunk's entering state is in LDS
             frag_t<T> Sk[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) Sk[ks] = load_frag_lin<T>(&sST[x][32 * ks], g);
+            for (int ks = 0; ks < KS; ++ks) Sk[ks] = load8(&sST[x][(32 * ks + 8 * g) ^ xsw]);
             f32x4 accV = quad_to_f<T>(f.U);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) accV = mma(f.Wn[ks], Sk[ks], accV);  // V~ = U - W S
             __builtin_amdgcn_sched_barrier(0);
             LD::uw(nx, nb, w, l, sl);
             __builtin_amdgcn_sched_barrier(0);
-            *reinterpret_cast<quad_t<T> *>(&sVT[x][kpos(16 * w + 4 * g)]) = make_quad<T>(accV);
+            *reinterpret_cast<quad_t<T> *>(&sVT[x][kpos(16 * w + 4 * g) ^ xsw]) = make_quad<T>(accV);
             lds_barrier();  // V~ of the whole chunk is in LDS; S^T fully read
             frag_t<T> Vf[2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) Vf[ks] = load_frag_lin<T>(&sVT[x][32 * ks], g);
+            for (int ks = 0; ks < 2; ++ks) Vf[ks] = load8(&sVT[x][(32 * ks + 8 * g) ^ xsw]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 S[rt] *= f.gam[rt];                       // Diag(gamma^C) S
@@ -1385,7 +1390,7 @@ __global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-                *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g)]) = make_quad<T>(S[rt]);
+                *reinterpret_cast<quad_t<T> *>(&sST[x][kpos(16 * (w * RT + rt) + 4 * g) ^ xsw]) = make_quad<T>(S[rt]);
             // Prefix-state checkpoint after every ckpt_every-th chunk strictly inside the sequence.
             if (p.ckpt_every > 0 && (lc + 1) % p.ckpt_every == 0) {
                 const int j = (lc + 1) / p.ckpt_every - 1;
@@ -1422,7 +1427,7 @@ __global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
             lds_barrier();  // S^T of this chunk's entering state is in LDS
             frag_t<T> Sk[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) Sk[ks] = load_frag_lin<T>(&sST[x][32 * ks], g);
+            for (int ks = 0; ks < KS; ++ks) Sk[ks] = load8(&sST[x][(32 * ks + 8 * g) ^ xsw]);
             // The output is formed transposed, O^T = S^T (Gamma Q)^T + V~^T A^T: the same
             // fragments with the operand roles swapped, so each lane ends with four
             // consecutive columns of one token (one 8-byte store).
@@ -1435,7 +1440,7 @@ __global__ __launch_bounds__(512) void chain_kernel(PrefillParams p)
             lds_barrier();  // V~ of the whole chunk is in LDS
             frag_t<T> Vf[2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) Vf[ks] = load_frag_lin<T>(&sVT[x][32 * ks], g);
+            for (int ks = 0; ks < 2; ++ks) Vf[ks] = load8(&sVT[x][(32 * ks + 8 * g) ^ xsw]);
             accO = mma(Vf[0], f.Af[0], accO);             // + (A V~)^T
             accO = mma(Vf[1], mask_frag<T>(f.Af[1], amask), accO);
             __builtin_amdgcn_sched_barrier(0);
