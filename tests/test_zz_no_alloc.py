@@ -5,11 +5,12 @@ Each call is checked against kda_chunk_fwd on the same inputs (outputs, final
 states and, with the prologue, the convolution state): the two run the same
 kernels on the same data, so they must agree bit for bit.  Calls follow one
 another on one device, largest first, so every call after the first runs on
-an array that still holds the previous call's blocks: packed sequences over
-128 (sequence, head) pairs (one workgroup per pair in the chain), then a
-smaller batched call with the layer prologue and epilogue fused (its
+an array that still holds the previous call's workspace: packed sequences over
+128 (sequence, head) pairs at bf16 (pair mode: the chain inside the
+intra-chunk kernel, the array holding only the chunk table), then a smaller
+batched call with the layer prologue and epilogue fused (split design, its
 convolution state written by the intra-chunk stage), then a smaller float32
-call.  A shape beyond the array is rejected and leaves the
+call that runs on the blocks the second call left.  A shape beyond the array is rejected and leaves the
 output untouched."""
 import dataclasses
 
