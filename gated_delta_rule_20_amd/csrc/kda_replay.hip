@@ -23,6 +23,22 @@
 
 namespace kda {
 
+// One element loaded or stored through a buffer descriptor (bf16: 2 bytes, fp32: 4 bytes).
+template <typename T> __device__ __forceinline__ T elem_load(__amdgpu_buffer_rsrc_t rs, int off_bytes)
+{
+    if constexpr (sizeof(T) == 2)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(rs, off_bytes, 0, 0));
+    else
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(rs, off_bytes, 0, 0));
+}
+template <typename T> __device__ __forceinline__ void elem_store(__amdgpu_buffer_rsrc_t rs, int off_bytes, T v)
+{
+    if constexpr (sizeof(T) == 2)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), rs, off_bytes, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, off_bytes, 0, 0);
+}
+
 // Row-broadcast FMAs.  Lane l holds row 16 V + (l % 16) of a per-row operand
 // in kr; DPP row_newbcast:n hands every lane of a 16-lane row the value of
 // its lane n, so 16 FMAs cover 16 rows with no further LDS reads and in the
@@ -195,22 +211,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     T *const cstate = (FU && cw > 1) ? (T *)p.f.conv_state + nh * (size_t)((cw - 1) * CC) : nullptr;
     // Split staging: the history of this thread's channels stays in registers
     // (h0: query or value channel, h1: key channel), the carried state's rows
-    // loaded here and converted in the first block's staging, so that waiting
-    // for them does not hold back the first block's input loads.
-    T hr0[3], hr1[3];
+    // loaded in the first block's staging right after its first token group's
+    // inputs, so that waiting for them holds back nothing and they are not live
+    // (nor spilled) before.
     float h0[3] = {0.f, 0.f, 0.f}, h1[3] = {0.f, 0.f, 0.f};
-    if constexpr (SPLIT) {
-        const bool kr = t < DK;
-        const unsigned c0 = kr ? (unsigned)t : DK + (unsigned)t, c1 = DK + (unsigned)t;  // q and k, or v = 2 DK + (t - DK)
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            const int j = i - 4 + cw;
-            const bool in = pro && cstate && j >= 0;
-            const T *cr = in ? cstate + j * CC : nullptr;
-            hr0[i] = in ? cr[c0] : from_f<T>(0.f);
-            hr1[i] = (in && kr) ? cr[c1] : from_f<T>(0.f);
-        }
-    } else if constexpr (FU) {
+    if constexpr (!SPLIT && FU) {
         if (pro) {
 #pragma unroll
             for (int i = 0; i < 3; ++i) {     // slot i holds state row i - 4 + cw (if any)
@@ -241,13 +246,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
             const unsigned c0 = kr ? uch : 2u * DK + uch, c1 = DK + uch;  // conv channels: q and k, or v
             float w0[4] = {0.f, 0.f, 0.f, 0.f}, w1[4] = {0.f, 0.f, 0.f, 0.f};
             if (pro) {
-                if (base == 0) {
-#pragma unroll
-                    for (int i = 0; i < 3; ++i) {
-                        h0[i] = to_f<T>(hr0[i]);
-                        h1[i] = to_f<T>(hr1[i]);
-                    }
-                }
                 const float *wb = p.f.conv_weight + (size_t)h * CC * cw;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {  // tap i holds weight i - 4 + cw (if any)
@@ -289,6 +287,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
                     }
                     bt[jj] = ok ? to_f<T>(((const T *)(rep ? p.beta_r : p.beta))[row]) : 0.f;
                 }
+                if (pro && base == 0 && j0 == 0 && cstate) {  // the carried convolution state
+                    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+                        cstate, 0, (cw - 1) * CC * (int)sizeof(T), 0x00020000);
+#pragma unroll
+                    for (int i = 0; i < 3; ++i) {
+                        const int r = i - 4 + cw;  // slot i holds state row r (if any)
+                        if (r >= 0) {
+                            h0[i] = to_f<T>(elem_load<T>(crs, (r * CC + (int)c0) * (int)sizeof(T)));
+                            if (kr) h1[i] = to_f<T>(elem_load<T>(crs, (r * CC + (int)c1) * (int)sizeof(T)));
+                        }
+                    }
+                }
 #pragma unroll
                 for (int jj = 0; jj < SB; ++jj) {
                     const int j = j0 + jj;
@@ -309,13 +319,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
                         y0 = c0v * __builtin_amdgcn_rcpf(1.f + __expf(-c0v));
                         y1 = c1v * __builtin_amdgcn_rcpf(1.f + __expf(-c1v));
                         if (j == jc && cstate) {  // committed: carry the last cw - 1 pre-activations
+                            // through a descriptor over this (sequence, head)'s rows: the base stays
+                            // uniform and each store takes one 32-bit lane offset, so no per-lane
+                            // 64-bit address is kept live across the token loop
+                            const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+                                cstate, 0, (cw - 1) * CC * (int)sizeof(T), 0x00020000);
 #pragma unroll
                             for (int i = 0; i < 3; ++i) {
                                 const int r = i - 4 + cw;
                                 if (r >= 0) {
-                                    T *cr = cstate + r * CC;
-                                    cr[c0] = from_f<T>(h0[i]);
-                                    if (kr) cr[c1] = from_f<T>(h1[i]);
+                                    elem_store<T>(crs, (r * CC + (int)c0) * (int)sizeof(T), from_f<T>(h0[i]));
+                                    if (kr) elem_store<T>(crs, (r * CC + (int)c1) * (int)sizeof(T), from_f<T>(h1[i]));
                                 }
                             }
                         }
