@@ -19,20 +19,32 @@
 // §5.1.1 describes the production kernel as token-parallel stages plus a
 // head-parallel recurrence; the same split is used here, laid out for gfx950:
 //
-//   chunk_table_kernel   (packed sequences only) chunk offsets per sequence
-//                        and a longest-first sequence order.
-//   intra_chunk_kernel   one workgroup per (chunk, head): gate, cumsum,
+//   chunk_table_kernel   (packed sequences only) clamped spans, chunk offsets
+//                        per sequence and a longest-first sequence order.
+//   intra_chunk_kernel   persistent over (chunk, head) items: gate, cumsum,
 //                        sub-tile Gram products on MFMA, blocked triangular
-//                        inverse in fp32, U / W / A on MFMA.  It writes every
-//                        operand of the chain as a ready-to-issue MFMA
-//                        fragment (layout in Block below).
-//   chain_kernel         one workgroup per (sequence, head, 16-column slice of
-//                        d_v): walks the chunks in order with its slice of S
-//                        in fp32 registers; per chunk two dependent MFMA
-//                        products (W S, then K~^T V~) sit on the serial path
-//                        and the output products (Q+ S, A V~) beside them.
-//                        Columns of S evolve independently (V~ = U - W S acts
-//                        column by column), which licenses the split.
+//                        inverse in fp32, U / W / A on MFMA; with the layer
+//                        prologue (eq. (2)) the inputs are first convolved,
+//                        passed through Swish, L2-normalised (q, k) and Sigmoid
+//                        (beta) in registers.  In the split design it writes
+//                        every operand of the chain as a ready-to-issue MFMA
+//                        fragment (layout in Block below).  In pair mode (128
+//                        or more (sequence, head) pairs at bf16, d_k = 128, no
+//                        prologue) each workgroup walks whole pairs chunk by
+//                        chunk and runs the chain step itself from the chunk's
+//                        block in LDS: no chain kernel, no block in HBM.
+//   chain_kernel         split design, fewer than 128 pairs: one workgroup per
+//                        (sequence, head, 16-column slice of d_v), walking the
+//                        chunks in order with its slice of S in fp32 registers;
+//                        per chunk two dependent MFMA products (W S, then
+//                        K~^T V~) sit on the serial path and the output products
+//                        (Q+ S, A V~) beside them.  Columns of S evolve
+//                        independently (V~ = U - W S acts column by column),
+//                        which licenses the split.
+//   chain_wide_kernel    split design from 128 pairs (when pair mode does not
+//                        apply): one workgroup per (sequence, head), all d_v
+//                        columns, each chunk's block copied whole into LDS.
+//   gate_norm_kernel     the layer epilogue (eq. (6)) in place on o.
 //
 // Sub-tile references.  Let B_m be lam just before 16-token tile m (B_0 = 0).
 // For rows r in tile m and columns i in tile n <= m, exp(lam_r - lam_i) is
