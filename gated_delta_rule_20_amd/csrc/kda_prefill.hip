@@ -137,8 +137,8 @@ __global__ __launch_bounds__(table::THREADS) void chunk_table_kernel(const int32
 // and the raw inputs of its next item are loaded into registers while the
 // current item is computed.
 //
-// Elementwise layout: wave w owns 8 tokens of 16-token sub-tile w % 4 (the
-// first or second half, w / 4) and lane l owns the CPT channels CPT*l..
+// Elementwise layout: wave w owns 8 tokens of a 16-token sub-tile (the first
+// or second half, w / 4; see seg_tile) and lane l owns the CPT channels CPT*l..
 // (CPT = d_k/64) across those 8 tokens, so the chunk-local cumsum runs inside
 // each thread and only the eight half-tile totals are exchanged.  Log-decays
 // are kept in log2 units (one exp2 per factor).
@@ -223,10 +223,14 @@ __device__ __forceinline__ int colop_row(int m, int n)
     return (n == 0) ? (m == 2 ? 112 : 128) : 144;
 }
 
-// Eight waves; wave w owns the 8-token half-tile (segment) 2*(w % 4) + w / 4,
-// i.e. tokens seg_base(w) .. +7 of sub-tile w % 4.
+// Eight waves; wave w owns the first (w < 4) or second half of sub-tile
+// seg_tile(w), i.e. tokens seg_base(w) .. +7.  Waves 4-7 take the sub-tiles in
+// reverse order: the elementwise pass forms four column-operand rows per token
+// of tile 0, three of tile 1, two of tile 2 and one of tile 3, and waves w and
+// w + 4 usually share a SIMD, which then holds five either way.
 constexpr int IWAVES = 8, HT = SUB / 2;
-__device__ __forceinline__ int seg_base(int w) { return SUB * (w & 3) + HT * (w >> 2); }
+__device__ __forceinline__ int seg_tile(int w) { return w < 4 ? w : 7 - w; }
+__device__ __forceinline__ int seg_base(int w) { return SUB * seg_tile(w) + HT * (w >> 2); }
 
 // Raw inputs of one (chunk, head) in registers, unconverted (converting at
 // load time would make the wave wait for the loads): lane l of wave w holds
@@ -529,7 +533,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 
     const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 4, x = l & 15;
     const int ch0 = CPT * l;  // first channel of this lane in the elementwise phase
-    const int m0 = w & 3, hf = w >> 2, tb = seg_base(w);  // elementwise: tile, half, first token
+    const int m0 = seg_tile(w), hf = w >> 2, tb = seg_base(w);  // elementwise: tile, half, first token
 
     using PI = ProIn<T, DK, DV>;
     typedef typename PI::vu vu;
@@ -705,7 +709,7 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
         const __amdgpu_buffer_rsrc_t rsq = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.q + row0 * DK), 0, reck, 0x00020000);
         const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc((void *)((const T *)p.v + row0 * DV), 0, recv, 0x00020000);
         const int offk = ch0 * (int)sizeof(T), offv = CPV * l * (int)sizeof(T);
-        float lam2[HT][CPT];  // (lam_r - B_m) log2(e) for this wave's tokens (tile m = w % 4)
+        float lam2[HT][CPT];  // (lam_r - B_m) log2(e) for this wave's tokens (tile m = m0)
         {
             const float cz = -__expf(raw.alog) * LOG2E;  // exp(-e^A z) = exp2(cz z)
             const float gm2 = p.g_min * LOG2E;
@@ -784,20 +788,19 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
 #pragma unroll
             for (int r0 = 0; r0 < HT; ++r0) {
                 const int r = HT * hf + r0, tok = tb + r0;  // r: token within the tile
-                ku kr_, qr_, kc_, ke_, kx1_, kx2_;
+                ku kr_, qr_, kc_;
+                float kce[CPT];
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) {
                     const float kv = to_f<T>(raw.k[r0][cc]);
                     const float qv = p.scale * to_f<T>(raw.q[r0][cc]);
                     const float eR = __builtin_amdgcn_exp2f(lam2[r0][cc]);        // exp(lam_r - B_w) <= 1
                     const float eC = __builtin_amdgcn_rcpf(eR);  // exp(B_w - lam_r) <= e^80
-                    const float kr = kv * eR, qr = qv * eR, kcs = kv * eC, kce = kcs * eT[cc];
+                    const float kr = kv * eR, qr = qv * eR, kcs = kv * eC;
+                    kce[cc] = kcs * eT[cc];
                     kr_[cc] = from_f<T>(kr);
                     qr_[cc] = from_f<T>(qr);
                     kc_[cc] = from_f<T>(kcs);
-                    ke_[cc] = from_f<T>(kce);
-                    kx1_[cc] = from_f<T>(kce * eX1[cc]);
-                    kx2_[cc] = from_f<T>(kce * eX2[cc]);
                     kpv[cc][r0] = from_f<T>(kr * eBm[cc]);
                     ktv[cc][r0] = from_f<T>(kcs * eCB[cc]);
                 }
@@ -805,12 +808,20 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 *reinterpret_cast<ku *>(&sm.ops.KR[tok][cp]) = kr_;
                 *reinterpret_cast<ku *>(&sm.ops.QR[tok][cp]) = qr_;
                 *reinterpret_cast<ku *>(&sm.y.KC[tok][cp]) = kc_;
-                if (m0 < 3) *reinterpret_cast<ku *>(&sm.y.KC[64 + tok][cp]) = ke_;
+                // the off-diagonal column operands, formed only by the tiles that have
+                // them (wave-uniform branches)
+                auto put_col = [&](int row, const float *fac) {
+                    ku v_;
+#pragma unroll
+                    for (int cc = 0; cc < CPT; ++cc) v_[cc] = from_f<T>(fac ? kce[cc] * fac[cc] : kce[cc]);
+                    *reinterpret_cast<ku *>(&sm.y.KC[row][cp]) = v_;
+                };
+                if (m0 < 3) put_col(64 + tok, nullptr);
                 if (m0 == 0) {
-                    *reinterpret_cast<ku *>(&sm.y.KC[112 + r][cp]) = kx1_;
-                    *reinterpret_cast<ku *>(&sm.y.KC[128 + r][cp]) = kx2_;
+                    put_col(112 + r, eX1);
+                    put_col(128 + r, eX2);
                 }
-                if (m0 == 1) *reinterpret_cast<ku *>(&sm.y.KC[144 + r][cp]) = kx1_;
+                if (m0 == 1) put_col(144 + r, eX1);
                 raw.g[r0] = buf_load<ku>(rsg, offk + r0 * rowk);
                 raw.k[r0] = buf_load<ku>(rsk, offk + r0 * rowk);
                 raw.q[r0] = buf_load<ku>(rsq, offk + r0 * rowk);
