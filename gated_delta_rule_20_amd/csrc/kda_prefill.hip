@@ -450,9 +450,20 @@ __device__ __forceinline__ bool next_item(const PrefillParams &p, int &i, int &c
     return false;
 }
 
-// Pair mode: workgroup b takes the (sequence, head) pairs of rank b, b + G, ...
-// (G = gridDim.x; ranks in the chunk table's longest-first order) and walks
-// each pair's chunks in order.  pair_of: the pair of rank r; false past the last.
+// Pair mode: workgroup b walks one (sequence, head) pair per round k, of rank
+// pair_rank(k) in the chunk table's longest-first order, and each pair's chunks
+// in order.  Round k deals ranks kG .. kG + G - 1 (G = gridDim.x) to the
+// workgroups forwards when k is even and backwards when k is odd, so that the
+// longest pairs of one round and the shortest of the next meet on one
+// workgroup; on the packed 64-sequence workload the busiest workgroup then
+// carries 2% more chunks than the mean instead of 11% with a plain stride.
+// Ranks grow with k for every workgroup.  pair_of: the pair of rank r; false
+// past the last.
+__device__ __forceinline__ int pair_rank(int k)
+{
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    return k * G + ((k & 1) ? G - 1 - b : b);
+}
 __device__ __forceinline__ bool pair_of(const PrefillParams &p, int r, int &s, int &h, int &start, int &slen, int &nch)
 {
     if (r >= p.N * p.H) return false;
@@ -472,17 +483,17 @@ __device__ __forceinline__ bool pair_of(const PrefillParams &p, int r, int &s, i
     return true;
 }
 
-// The chunk after (r, lc): the pair's next chunk, else chunk 0 of this
+// The chunk after (round k, lc): the pair's next chunk, else chunk 0 of this
 // workgroup's next pair that has chunks; its token range.  False when done.
-__device__ __forceinline__ bool pair_next(const PrefillParams &p, int &r, int &lc, int &s, int &h, int &start,
+__device__ __forceinline__ bool pair_next(const PrefillParams &p, int &k, int &lc, int &s, int &h, int &start,
                                           int &slen, int &nch, int &tok0, int &len)
 {
     if (lc + 1 < nch) {
         ++lc;
     } else {
         lc = 0;
-        for (r += gridDim.x;; r += gridDim.x) {
-            if (!pair_of(p, r, s, h, start, slen, nch)) return false;
+        for (++k;; ++k) {
+            if (!pair_of(p, pair_rank(k), s, h, start, slen, nch)) return false;
             if (nch > 0) break;
         }
     }
@@ -546,15 +557,15 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
     f32x4 S[NR][CT];  // pair mode, waves w < NCW: the pair's state, columns 16 w + x
     if constexpr (PAIR) {
         // pairs without tokens: the final state is the initial one
-        for (int r = blockIdx.x;; r += gridDim.x) {
+        for (int k = 0;; ++k) {
             int s_, h_, st_, sl_, n_;
-            if (!pair_of(p, r, s_, h_, st_, sl_, n_)) break;
+            if (!pair_of(p, pair_rank(k), s_, h_, st_, sl_, n_)) break;
             if (n_ == 0 && p.hT) {
                 const size_t sb = ((size_t)s_ * p.H + h_) * DK * DV;
                 for (int e = t; e < DK * DV; e += 64 * IWAVES) p.hT[sb + e] = p.h0 ? p.h0[sb + e] : 0.f;
             }
         }
-        i = (int)blockIdx.x - (int)gridDim.x;
+        i = -1;  // pair mode: i counts the workgroup's rounds
         have = pair_next(p, i, lc, sq, h, pst, slen, nch, tok0, len);
     } else {
         have = PRO ? next_item_seq(p, i, c, h, tok0, len, sq, lc, slen) : next_item(p, i, c, h, tok0, len);
