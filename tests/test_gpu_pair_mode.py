@@ -114,3 +114,12 @@ def test_pair_mode_checkpoints():
                 assert torch.isnan(ck[s, j]).all(), (s, j)
     print(f"{checked} slots, worst checkpoint rel err {worst:.3e}")
     assert checked > 20
+
+
+def test_pair_mode_partial_odd_round():
+    """868 pairs (217 sequences x 4 heads): the workgroups take their pairs in
+    rounds of 256, forwards on even rounds and backwards on odd ones, and the
+    fourth round (odd) holds only 100 pairs, all on the high-numbered
+    workgroups.  Every pair's output and final state against the oracle."""
+    inp = _packed(_lengths(217, 17, hi=160), H=4, seed=46)
+    _check(inp)
