@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import workloads as W
-from kda_testutil import TOL, np64, rel_err
+from kda_testutil import TOL, np64, oracle_prefill, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -80,7 +80,7 @@ def test_segment_map_is_affine():
 def test_segments_merged_in_order_reproduce_one_pass():
     """d = 128, 4 heads, 2048 tokens split into 4 segments of 512: local (M, S~) per
     segment, prefix merge, re-run from the merged entering states; outputs and
-    final state match the single pass."""
+    final state match the single pass and the fp64 oracle's single pass."""
     inp = _inputs()
     T = inp["q"].shape[1]
     P = 4
@@ -98,3 +98,9 @@ def test_segments_merged_in_order_reproduce_one_pass():
     e_s = rel_err(np64(S_in), np64(h_ref))
     print(f"KCP rel err o={e_o:.3e} state={e_s:.3e}")
     assert e_o <= TOL[torch.bfloat16] and e_s <= TOL[torch.bfloat16]
+    ro, rh, _ = oracle_prefill(inp, z_mode=False)  # log-decay mode, as the calls above
+    H, Dv = inp["q"].shape[2], inp["v"].shape[-1]
+    e_oo = rel_err(np64(torch.cat(outs, 1)).reshape(-1, H, Dv), ro)
+    e_os = rel_err(np64(S_in), rh)
+    print(f"KCP against the oracle: rel err o={e_oo:.3e} state={e_os:.3e}")
+    assert e_oo <= TOL[torch.bfloat16] and e_os <= TOL[torch.bfloat16]
