@@ -11,7 +11,8 @@ design (a few (sequence, head) pairs) and in pair mode (128 pairs or more):
   unit vectors of the standard basis (orthonormal, and exact in bf16) with
   q_t = k_t, so that every product in the chunked form is exact and
   o_t = v_t, the final state holds v_i in row i's axis and zeros elsewhere:
-  compared bit for bit.
+  compared bit for bit; the same conditions also for 64 decode steps and for
+  speculative windows (replayed tokens, then new tokens with any commit count).
 
 Log-decay mode throughout (g is given, A_log = NULL)."""
 import dataclasses
@@ -141,3 +142,75 @@ def test_exact_retrieval_bitwise(mode):
     assert torch.equal(o, inp["v"]), float((o.float() - inp["v"].float()).abs().max())
     assert torch.equal(hT.cpu(), torch.from_numpy(S_ref))
     _check_oracle(inp)
+
+
+def _basis_keys(r, N, T, H, Dk):
+    """[N, T, H, Dk] keys: for each (sequence, head), T distinct signed basis
+    vectors (a random permutation of the axes); also their axes and signs."""
+    axes = np.stack([np.stack([r.permutation(Dk)[:T] for _ in range(H)], 1) for _ in range(N)])  # [N, T, H]
+    signs = r.choice([-1.0, 1.0], size=(N, T, H))
+    keys = np.zeros((N, T, H, Dk), np.float32)
+    n, t, h = np.meshgrid(np.arange(N), np.arange(T), np.arange(H), indexing="ij")
+    keys[n, t, h, axes] = signs
+    return keys, axes, signs
+
+
+def _write_rows(S, axes, signs, v):
+    """S[n, h, axes[n, t, h]] = signs * v[n, t, h] for every t (host arrays)."""
+    N, T, H = axes.shape
+    for t in range(T):
+        n, h = np.meshgrid(np.arange(N), np.arange(H), indexing="ij")
+        S[n, h, axes[:, t, :]] = signs[:, t, :, None] * v[:, t, :]
+
+
+def test_decode_exact_retrieval_bitwise():
+    """The decode step under the same exact conditions (alpha = beta = 1, S_0 = 0,
+    q = k = distinct signed basis vectors): 64 steps over 8 sequences x 4 heads,
+    every step returns o = v and the state ends with +-v in the written rows and
+    zeros elsewhere, bit for bit."""
+    import gated_delta_rule_20_amd as kda
+    N, H, Dk, Dv, steps = 8, 4, 128, 128, 64
+    r = np.random.default_rng(84)
+    gen = torch.Generator(device="cuda").manual_seed(84)
+    keys, axes, signs = _basis_keys(r, N, steps, H, Dk)
+    v = torch.randn(N, steps, H, Dv, generator=gen, device="cuda").to(torch.bfloat16)
+    state = torch.zeros(N, H, Dk, Dv, device="cuda")
+    g = torch.zeros(N, H, Dk, dtype=torch.bfloat16, device="cuda")   # log-decay 0: alpha = 1
+    beta = torch.ones(N, H, dtype=torch.bfloat16, device="cuda")
+    kk = torch.from_numpy(keys).to("cuda", torch.bfloat16)
+    for t in range(steps):
+        k = kk[:, t].contiguous()
+        o = kda.recurrent_step(k, k, v[:, t].contiguous(), g, beta, state)
+        torch.cuda.synchronize()
+        assert torch.equal(o, v[:, t]), (t, float((o.float() - v[:, t].float()).abs().max()))
+    S_ref = np.zeros((N, H, Dk, Dv), np.float32)
+    _write_rows(S_ref, axes, signs, v.float().cpu().numpy())
+    assert torch.equal(state.cpu(), torch.from_numpy(S_ref))
+
+
+@pytest.mark.parametrize("n_commit", [0, 5, 8])
+def test_replay_exact_retrieval_bitwise(n_commit):
+    """The speculative window under the same exact conditions: 6 cached tokens
+    replayed, then 8 new tokens with outputs, n_commit of them committed: every
+    new token's output is its v, and the state written back holds the replayed
+    and committed tokens' rows only, bit for bit."""
+    import gated_delta_rule_20_amd as kda
+    N, H, Dk, Dv, Tr, Tn = 8, 4, 128, 128, 6, 8
+    r = np.random.default_rng(85 + n_commit)
+    gen = torch.Generator(device="cuda").manual_seed(85 + n_commit)
+    keys, axes, signs = _basis_keys(r, N, Tr + Tn, H, Dk)
+    kk = torch.from_numpy(keys).to("cuda", torch.bfloat16)
+    v = torch.randn(N, Tr + Tn, H, Dv, generator=gen, device="cuda").to(torch.bfloat16)
+    g = torch.zeros(N, Tr + Tn, H, Dk, dtype=torch.bfloat16, device="cuda")
+    beta = torch.ones(N, Tr + Tn, H, dtype=torch.bfloat16, device="cuda")
+    new = lambda x: x[:, Tr:].contiguous()
+    old = lambda x: x[:, :Tr].contiguous()
+    state = torch.zeros(N, H, Dk, Dv, device="cuda")
+    o = kda.recurrent_replay(new(kk), new(kk), new(v), new(g), new(beta), state,
+                             replay=(old(kk), old(v), old(g), old(beta)), n_commit=n_commit)
+    torch.cuda.synchronize()
+    assert torch.equal(o, new(v)), float((o.float() - new(v).float()).abs().max())
+    S_ref = np.zeros((N, H, Dk, Dv), np.float32)
+    kept = Tr + n_commit
+    _write_rows(S_ref, axes[:, :kept], signs[:, :kept], v[:, :kept].float().cpu().numpy())
+    assert torch.equal(state.cpu(), torch.from_numpy(S_ref))
