@@ -14,7 +14,8 @@ design (a few (sequence, head) pairs) and in pair mode (128 pairs or more):
   compared bit for bit; the same conditions also for 64 decode steps and for
   speculative windows (replayed tokens, then new tokens with any commit count).
 
-Log-decay mode throughout (g is given, A_log = NULL)."""
+Log-decay mode throughout (g is given, A_log = NULL), except for the in-place
+resume check at the end (final state written over the initial one)."""
 import dataclasses
 
 import numpy as np
@@ -214,3 +215,23 @@ def test_replay_exact_retrieval_bitwise(n_commit):
     kept = Tr + n_commit
     _write_rows(S_ref, axes[:, :kept], signs[:, :kept], v[:, :kept].float().cpu().numpy())
     assert torch.equal(state.cpu(), torch.from_numpy(S_ref))
+
+
+@pytest.mark.parametrize("mode,Dk", [("split", 128), ("pair", 128), ("pair", 64)])
+def test_in_place_resume(mode, Dk):
+    """final_state given as the very tensor of initial_state (in-place resume, as
+    the header allows): outputs and state bit for bit equal to the call with a
+    separate final state.  ("pair", 64): 130 pairs at d_k = 64 take the wide
+    chain (pair mode needs d_k = 128)."""
+    import gated_delta_rule_20_amd as kda
+    inp = _inputs(mode, 86)
+    if Dk != 128:
+        inp["q"], inp["k"], inp["z"] = (inp[n][..., :Dk].contiguous() for n in ("q", "k", "z"))
+        inp["h0"] = inp["h0"][:, :, :Dk].contiguous()
+    o1, h1 = gpu_prefill(inp, z_mode=True)
+    S = inp["h0"].clone()
+    o2, h2 = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["z"], inp["beta"], A_log=inp["A_log"],
+                           g_min=inp["g_min"], cu_seqlens=inp["cu_seqlens"], initial_state=S, final_state=S)
+    torch.cuda.synchronize()
+    assert h2.data_ptr() == S.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(h1, S)
