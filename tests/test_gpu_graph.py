@@ -115,3 +115,35 @@ def test_decode_step_graph_replays():
         torch.cuda.synchronize()
         _same(f"o (step {i})", o, o_ref)
         _same(f"state (step {i})", state, ref_state)
+
+
+def test_speculative_window_graph_replays():
+    """kda_recurrent_replay (replayed drafts of a cached window, then a new
+    window, bonus committed) captured once; four replays on fresh windows and
+    accepted counts, against eager calls on a copy of the state."""
+    import gated_delta_rule_20_amd as kda
+    w = dataclasses.replace(W.WORKLOADS["decode_512_spec"], seed=320)
+    d = W.make_spec_decode(w, device="cuda", N=8, H=4, calls=4)
+    names = ("k_r", "v_r", "z_r", "beta_r", "n_replay", "q", "k", "v", "z", "beta")
+    static = {n: d["calls"][0][n].clone() for n in names}
+    state = d["state"].clone()
+    o = torch.empty_like(static["v"])
+
+    def call():
+        kda.recurrent_replay(static["q"], static["k"], static["v"], static["z"], static["beta"], state,
+                             replay=(static["k_r"], static["v_r"], static["z_r"], static["beta_r"]),
+                             n_replay=static["n_replay"], n_commit=1, A_log=d["A_log"], g_min=d["g_min"], out=o)
+
+    g = _capture(call)  # the set-up run advanced `state`: restart from the initial state
+    state.copy_(d["state"])
+    ref_state = d["state"].clone()
+    for i, c in enumerate(d["calls"]):
+        for n in names:
+            static[n].copy_(c[n])
+        g.replay()
+        o_ref = kda.recurrent_replay(c["q"], c["k"], c["v"], c["z"], c["beta"], ref_state,
+                                     replay=(c["k_r"], c["v_r"], c["z_r"], c["beta_r"]), n_replay=c["n_replay"],
+                                     n_commit=1, A_log=d["A_log"], g_min=d["g_min"])
+        torch.cuda.synchronize()
+        _same(f"o (call {i})", o, o_ref)
+        _same(f"state (call {i})", state, ref_state)
