@@ -7,12 +7,14 @@ are what a repeated token gives.  Checked against the fp64 oracle on the
 split design and in pair mode.
 
 A whole 64-token chunk on one key, with beta = 1 and no decay, is held to a
-looser bound than the 2e-2 of the workloads.  There the pseudo-values are
-differences of consecutive values (V~_r ~ v_r - v_(r-1)), and the output of
-token r sums them over the chunk's first r + 1 tokens (A_ri = q.k).  Each V~_r
-is rounded to bf16 twice on its way (U, then V~ as an MFMA operand), so the
-sum carries about sqrt(r + 1) independent roundings of relative size 2^-9:
-for r = 63 about 8 * 2 * 2^-9 * sqrt(2) ~ 0.044 of max|v|, which is what the
+looser bound than the 2e-2 of the workloads.  There T' = (I + L)^-1 Diag(beta)
+is close to the difference operator, the pseudo-values are differences of
+consecutive values (V~_r ~ v_r - v_(r-1)), and the output of token r sums them
+over the chunk's first r + 1 tokens (A_ri = q.k).  Each V~_r carries bf16
+roundings of relative size 2^-9: T''s subdiagonal -beta |k|^2 as an MFMA
+operand (so the difference no longer cancels exactly), U, and V~ as an
+operand.  The sum then carries about sqrt(r + 1) independent roundings: for
+r = 63 about 8 * 2 * 2^-9 * sqrt(2) ~ 0.044 of max|v|, which is what the
 kernels measure (2e-2 to 5e-2).  The test bounds it at 0.1, which guards
 against a blow-up, not against this accumulation."""
 import dataclasses
