@@ -1043,14 +1043,24 @@ __global__ __launch_bounds__(512) void intra_chunk_kernel(PrefillParams p)
                 for (int d = 1; d < 4; ++d) {
                     if (n + d > 3) break;
                     const int m = n + d;
+                    // the step's L blocks and D_m, read together before its products (the
+                    // previous step's stores to Tp keep the compiler from reading earlier)
+                    f32x4 La[3];
+#pragma unroll
+                    for (int qd = 0; qd < d; ++qd)
+                        La[qd] = *reinterpret_cast<const f32x4 *>(&L[16 * m + x][(16 * (n + qd) + 4 * g) ^ swz_l(x)]);
+                    f32x4 dm = *reinterpret_cast<const f32x4 *>(dblk(sm, m) + x * LP + ((4 * g) ^ swz_l(x)));
+                    // (held in place: the compiler would otherwise sink each read to its
+                    // product and wait for it there)
+#pragma unroll
+                    for (int qd = 0; qd < d; ++qd) asm volatile("" : "+v"(La[qd]));
+                    asm volatile("" : "+v"(dm));
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int qd = 0; qd < d; ++qd) {
-                        const f32x4 a = *reinterpret_cast<const f32x4 *>(&L[16 * m + x][(16 * (n + qd) + 4 * g) ^ swz_l(x)]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], Tr[qd][i], acc, 0, 0, 0);
+                        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(La[qd][i], Tr[qd][i], acc, 0, 0, 0);
                     }
-                    const f32x4 dm = *reinterpret_cast<const f32x4 *>(dblk(sm, m) + x * LP + ((4 * g) ^ swz_l(x)));
                     f32x4 tm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) tm = __builtin_amdgcn_mfma_f32_16x16x4f32(dm[i], acc[i], tm, 0, 0, 0);
